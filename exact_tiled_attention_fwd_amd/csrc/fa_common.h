@@ -1,0 +1,55 @@
+// Shared device types and helpers for the gfx950 attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+namespace fa {
+
+// Mask modes, mirroring fa_mask.
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_LOCAL = 2 };
+
+// Whether key j takes part in query i's softmax (same predicate as the
+// C-ABI documents: causal j <= i, band |i - j| <= window).
+template <int MASK>
+__device__ __forceinline__ bool allowed(int i, int j, int window) {
+  if constexpr (MASK == MASK_CAUSAL) return j <= i;
+  else if constexpr (MASK == MASK_LOCAL) return (i - j <= window) && (j - i <= window);
+  else return true;
+}
+
+// Key range [lo, hi) any query of [q0, q1) can see under the mask.
+template <int MASK>
+__device__ __forceinline__ void key_range(int q0, int q1, int N, int window, int& lo, int& hi) {
+  lo = 0;
+  hi = N;
+  if constexpr (MASK == MASK_CAUSAL) hi = q1 < N ? q1 : N;
+  if constexpr (MASK == MASK_LOCAL) {
+    lo = q0 - window > 0 ? q0 - window : 0;
+    long long h = (long long)q1 + window;  // last query q1-1 sees keys <= q1-1+window
+    hi = h < N ? (int)h : N;
+  }
+}
+
+// Whether every (query, key) pair with query in [q0, q1) and key in
+// [k0, k1) is allowed (so the tile needs no per-element mask).
+template <int MASK>
+__device__ __forceinline__ bool tile_full(int q0, int q1, int k0, int k1, int window) {
+  if constexpr (MASK == MASK_CAUSAL) return k1 - 1 <= q0;
+  else if constexpr (MASK == MASK_LOCAL) {
+    int a = (q1 - 1) - k0, b = (k1 - 1) - q0;
+    return (a > b ? a : b) <= window;
+  } else return true;
+}
+
+}  // namespace fa

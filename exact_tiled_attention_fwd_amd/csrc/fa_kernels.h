@@ -1,0 +1,74 @@
+// Internal kernel launch interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "fa_common.h"
+
+namespace fa {
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int BH;
+  int N;
+  int n_qtiles;       // filled by the launcher
+  int window;
+  float scale_log2;   // |scale| * log2(e), > 0
+  float scale_abs;    // |scale| (0 becomes 1 with Q zeroed)
+  unsigned q_and;     // Q bits are (q & q_and) ^ q_xor: identity, negate or zero
+  unsigned q_xor;
+};
+
+struct FwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int BH;
+  int N;
+  int d;
+  int window;
+  float scale;
+};
+
+// cfg selects a tile configuration (0 = default); tuning only.
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdF32Args& a, int mask, hipStream_t stream);
+
+}  // namespace fa
+
+namespace fa {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;   // workspace: [BH][N][d] float32 dQ accumulator
+  float* delta;    // workspace: [BH][N] float32, D_i = <dO_i, O_i>
+  int BH;
+  int N;
+  int d;
+  int window;
+  float scale;       // signed scale as given
+  float scale_log2;  // |scale| * log2(e) (bf16 path)
+  float scale_abs;
+  unsigned q_and;    // bf16 path: Q bits are (q & q_and) ^ q_xor
+  unsigned q_xor;
+};
+
+// Workspace layout shared by fa_bwd_workspace_bytes and the launcher.
+size_t bwd_workspace_bytes(int BH, int N, int d);
+void bwd_workspace_split(void* ws, int BH, int N, int d, float** dq_acc, float** delta);
+
+hipError_t launch_bwd(const BwdArgs& a, int bf16, int mask, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,113 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library for MI355X (gfx950).
+ *
+ * The operation is exact attention, O = softmax(scale * Q K^T) V, per
+ * (batch, head) slice, as defined in "Flash attention and efficient attention
+ * — Hinglish notes", section "The Standard Attention Problem" (scores, row
+ * softmax, weighted sum of values). The forward pass streams K/V tiles
+ * through on-chip memory and merges per-tile row maximum m and row sum l with
+ * the rescaling rule of that page's "Derivation: Incremental Softmax"
+ * (Steps 2–3), so the N x N score matrix never reaches device memory. The
+ * backward pass recomputes scores and probabilities on chip from Q, K and the
+ * saved log-sum-exp, as the same page's "Backward Pass: Recomputation" says.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, contiguous, row-major [B][H][N][d] (d fastest);
+ *    LSE is [B][H][N] float32. All pointers are DEVICE pointers of the
+ *    current HIP device, 16-byte aligned.
+ *  - dtype FA_BF16: bfloat16 storage, products accumulated in float32,
+ *    d in {64, 128}. dtype FA_F32: float32 storage and arithmetic,
+ *    1 <= d <= 128.
+ *  - scale: any finite float (0 and negative values are allowed).
+ *  - mask: FA_MASK_NONE; FA_MASK_CAUSAL (key j allowed iff j <= query i,
+ *    square, top-left aligned); FA_MASK_LOCAL (allowed iff |i - j| <= window,
+ *    the symmetric band of the notes' "Worked example Local Attention
+ *    Window", whose 6 x 6 matrix is window = 1). window is ignored unless
+ *    mask == FA_MASK_LOCAL and must then be >= 0. Every query row keeps at
+ *    least its own key, so no row is empty.
+ *  - Ownership: the caller owns and allocates every buffer; the library
+ *    keeps no pointer after a call returns and allocates no device memory.
+ *  - Outputs are fully overwritten and must not overlap any input.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
+ *    default stream) and the call returns without synchronizing. Argument
+ *    errors are reported before anything is enqueued; a launch failure is
+ *    reported as FA_ERR_LAUNCH; faults during execution surface at the
+ *    caller's next synchronization.
+ *  - Limits: B, H, N >= 1; B*H <= 2^31-1; N*d <= 2^31-1.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a size limit exceeded */
+    FA_ERR_DTYPE = 3,     /* unknown dtype */
+    FA_ERR_HEADDIM = 4,   /* d not supported for this dtype */
+    FA_ERR_MASK = 5,      /* unknown mask, or window < 0 with FA_MASK_LOCAL */
+    FA_ERR_SCALE = 6,     /* scale is NaN or infinite */
+    FA_ERR_ALIGN = 7,     /* a pointer is not 16-byte aligned */
+    FA_ERR_WORKSPACE = 8, /* workspace missing or smaller than required */
+    FA_ERR_LAUNCH = 9,    /* the HIP runtime rejected a kernel launch */
+    FA_ERR_ALIAS = 10     /* an output buffer overlaps an input buffer */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_LOCAL = 2 } fa_mask;
+
+/*
+ * Forward pass.
+ *   q, k, v : inputs [B][H][N][d] in `dtype`.
+ *   o       : output [B][H][N][d] in `dtype`: O_i = sum_j P_ij v_j with
+ *             P_ij = exp(z_ij - LSE_i) over allowed j, z_ij = scale <q_i, k_j>.
+ *   lse     : output [B][H][N] float32: LSE_i = m_i + ln l_i in natural-log
+ *             units of the scaled, masked logits (m_i the row maximum, l_i the
+ *             row sum of exp(z_ij - m_i)); the backward pass consumes it.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, fa_dtype dtype,
+                 float scale, fa_mask mask, int window, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem (a float32
+ * row-statistics buffer and a float32 dQ accumulator). Returns 0 for an
+ * invalid problem description.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Backward pass of the forward above for the loss whose gradient w.r.t. O is
+ * dout. Recomputes P_ij = exp(z_ij - LSE_i) on chip (nothing N x N is read or
+ * written) and returns
+ *   dV_j = sum_i P_ij dO_i,
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+ *   with dS_ij = P_ij (<dO_i, v_j> - D_i) and D_i = <dO_i, O_i>.
+ *   q, k, v, o, dout : inputs [B][H][N][d] in `dtype` (o and lse as written
+ *                      by fa_fwd with the same scale and mask).
+ *   lse              : input [B][H][N] float32.
+ *   dq, dk, dv       : outputs [B][H][N][d] in `dtype`.
+ *   workspace        : device buffer of at least
+ *                      fa_bwd_workspace_bytes(...) bytes, owned by the caller,
+ *                      contents ignored on entry and undefined on return.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int N, int d, fa_dtype dtype,
+                 float scale, fa_mask mask, int window, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */
