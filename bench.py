@@ -1,0 +1,221 @@
+"""Bench: exact tiled attention on one MI355X.
+
+One step = one pass of the whole hot path over one batch: fa_fwd (writes O
+and LSE) followed by fa_bwd (recomputes P from LSE, writes dQ, dK, dV), on
+the causal bf16 workload [B=2, H=16, N=4096, d=128] with seeded synthetic
+inputs already resident in device memory. The JSON line also carries the
+forward-only figure of the causal [2, 16, 8192, 128] workload, the roofline
+of the dominant kernel, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s dense)
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def attn_pairs(N, mask, window):
+    """Number of allowed (query, key) pairs per head."""
+    if mask == "causal":
+        return N * (N + 1) // 2
+    if mask == "local":
+        w = min(window, N - 1)
+        return N * (2 * w + 1) - w * (w + 1)
+    return N * N
+
+
+def fwd_flops(w):
+    """Algorithmic forward FLOPs: 4*B*H*N^2*d, halved under a causal mask;
+    band masks count the allowed pairs (4*B*H*pairs*d)."""
+    B, H, N, d = w.shape
+    if w.mask == "causal":
+        return 4.0 * B * H * N * N * d / 2
+    if w.mask == "local":
+        return 4.0 * B * H * attn_pairs(N, "local", w.window) * d
+    return 4.0 * B * H * N * N * d
+
+
+def bwd_flops(w):
+    """Algorithmic backward FLOPs: five N^2 d contractions (QK^T recompute,
+    dO V^T, P^T dO, dS^T Q, dS K) = 10*B*H*N^2*d, halved under causal."""
+    return 2.5 * fwd_flops(w)
+
+
+def fwd_bytes(w):
+    B, H, N, d = w.shape
+    es = 2 if w.dtype == "bf16" else 4
+    return 4 * B * H * N * d * es + B * H * N * 4  # Q, K, V read, O written + LSE
+
+
+def bwd_bytes(w):
+    B, H, N, d = w.shape
+    es = 2 if w.dtype == "bf16" else 4
+    # read Q, K, V, O, dO, LSE; write dQ, dK, dV
+    return 8 * B * H * N * d * es + B * H * N * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-headline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
+              "communication, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_tiled_attention_fwd_amd as fa
+    from exact_tiled_attention_fwd_amd.synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+
+    have_bwd = True
+    name = args.workload or "bf16_causal_bwd_b2h16_n4096_d128"
+    w = WORKLOADS[name]
+    inp = make_inputs(w, with_dout=True)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    B, H, N, d = w.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d, q.dtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.mask, w.window, stream)
+
+    def bwd():
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, w.mask, w.window, stream)
+
+    def step():
+        fwd()
+        if have_bwd:
+            bwd()
+
+    def timed(fn, reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps  # ms
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = timed(step, args.steps)
+    wall = time.perf_counter() - t0
+    flops_step = fwd_flops(w) + (bwd_flops(w) if have_bwd else 0.0)
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    # per-kernel-unit launch durations over the same number of launches
+    ms_fwd = timed(fwd, args.steps)
+    kernels = {"fa_fwd": (ms_fwd, fwd_flops(w), fwd_bytes(w))}
+    if have_bwd:
+        ms_bwd = timed(bwd, args.steps)
+        kernels["fa_bwd"] = (ms_bwd, bwd_flops(w), bwd_bytes(w))
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    ms_dom, fl_dom, by_dom = kernels[dom]
+    achieved = fl_dom / (ms_dom * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": dom,
+                "algorithmic_flop_per_launch": fl_dom,
+                "avg_launch_us": round(ms_dom * 1e3, 2)}
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s (bf16) + % of MI355X MFMA peak, N=2k-16k",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded torch.randn, bf16-rounded)",
+        "config": {"workload": name, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
+                   "mask": w.mask, "window": w.window if w.mask == "local" else None,
+                   "step": "fa_fwd + fa_bwd" if have_bwd else "fa_fwd",
+                   "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "fwd_tflops": round(fwd_flops(w) / (ms_fwd * 1e-3) / 1e12, 1),
+                   "bwd_tflops": round(bwd_flops(w) / (kernels["fa_bwd"][0] * 1e-3) / 1e12, 1)
+                   if have_bwd else None,
+                   "wall_s_timed": round(wall, 3)},
+        "roofline": roofline,
+    }
+
+    if not args.no_headline:
+        hw = WORKLOADS["bf16_causal_b2h16_n8192_d128"]
+        hin = make_inputs(hw)
+        hq, hk, hv = (hin[n].to(dev) for n in ("q", "k", "v"))
+        ho = torch.empty_like(hq)
+        hl = torch.empty(hq.shape[:-1], dtype=torch.float32, device=dev)
+
+        def hfwd():
+            fa.fa_fwd(hq, hk, hv, ho, hl, hw.scale, hw.mask, hw.window, stream)
+        for _ in range(args.warmup):
+            hfwd()
+        hms = timed(hfwd, args.steps)
+        ht = fwd_flops(hw) / (hms * 1e-3) / 1e12
+        out["headline_forward"] = {
+            "workload": hw.name, "tflops": round(ht, 1),
+            "frac_of_peak": round(ht / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(hms * 1e3, 2),
+            "hbm_gbs": round(fwd_bytes(hw) / (hms * 1e-3) / 1e9, 1)}
+        del hq, hk, hv, ho, hl
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, have_bwd)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, have_bwd):
+    """The CPU oracle (plain double C, OpenMP) on one (batch, head) slice of
+    the same workload: dense forward over all rows plus, when the step has a
+    backward, the dense backward of that slice."""
+    import numpy as np
+    import oracle
+    B, H, N, d = w.shape
+    sl = {n: inp[n].reshape(B * H, N, d)[:1] for n in ("q", "k", "v", "dout")}
+    t0 = time.perf_counter()
+    oracle.fwd_dense(sl["q"], sl["k"], sl["v"], w.scale, w.mask, w.window)
+    if have_bwd:
+        oracle.bwd_dense(sl["q"], sl["k"], sl["v"], sl["dout"], w.scale, w.mask, w.window)
+    sec = time.perf_counter() - t0
+    one = type(w)(**{**w.__dict__, "B": 1, "H": 1})
+    flops = fwd_flops(one) + (bwd_flops(one) if have_bwd else 0.0)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"one (b,h) slice [1,1,{N},{d}] of {w.name}: dense forward"
+                      + (" + dense backward" if have_bwd else "") + ", float64"}
+
+
+if __name__ == "__main__":
+    main()

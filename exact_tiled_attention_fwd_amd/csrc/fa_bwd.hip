@@ -1,5 +1,644 @@
+// Backward exact attention by recomputation.
+//
+// The notes ("Flash attention and efficient attention — Hinglish notes",
+// "Backward Pass: Recomputation") only say that S and P are recomputed on
+// chip from Q, K, V instead of being read back from device memory. The
+// gradient of sum(dO * O) follows from the definition by the chain rule:
+//   P_ij = exp(z_ij - LSE_i),      D_i  = <dO_i, O_i>
+//   dV_j = sum_i P_ij dO_i,        dS_ij = P_ij (<dO_i, v_j> - D_i)
+//   dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j
+// where LSE is the forward's saved log-sum-exp.
+//
+// Three launches on the caller's stream, no atomics, deterministic:
+//  1. preprocess: D_i for every row (reads O and dO once).
+//  2. dK/dV, key-major: a workgroup owns a block of keys (K, V kept in
+//     registers as MFMA B operands) and streams every query tile that sees
+//     them through LDS. S = Q K^T puts the key on the lane, so P^T and dS^T
+//     are already the A operands of dV += P^T dO and dK += dS^T Q; the B
+//     operands (dO, Q with the query along the lane vector) come from
+//     ds_read_b64_tr_b16.
+//  3. dQ, query-major (the forward's layout): S^T = K Q^T and dP^T = V dO^T
+//     put the query on the lane, so LSE_i and D_i are per-lane scalars, and
+//     dS^T is the B operand of dQ^T += K^T dS^T (K read transposed).
+// Recomputing S and dP in step 3 costs two extra contractions (7 instead of
+// the 5 the gradient needs), the price of determinism without atomics.
 #include "fa_common.h"
 #include "fa_kernels.h"
+
 namespace fa {
-hipError_t launch_bwd(const BwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
+
+// XOR swizzle of 16-byte chunks for tiles read both as rows (16-byte
+// reads, 32 rows at one column) and transposed (ds_read_b64_tr_b16,
+// 8 rows x 64 bytes): both patterns are bank-conflict free.
+template <int D>
+__device__ __forceinline__ int swz_dual(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | ((x >> 1) & 3);
+  }
 }
+
+__device__ __forceinline__ void xcd_remap(int& w, int total) {
+  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
+}
+
+// ---------------------------------------------------------------- preprocess
+// D_i = <dO_i, O_i> in float32; d/8 threads per row, 16 bytes each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const bf16* __restrict__ o,
+                                                           const bf16* __restrict__ dout,
+                                                           float* __restrict__ delta, long rows) {
+  constexpr int TPR = D / 8;
+  const long row = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 x = *(const bf16x8*)(o + row * D + part * 8);
+    const bf16x8 y = *(const bf16x8*)(dout + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK / dV
+template <int D, int NW, int BRQ, int MASK>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BC = NW * 32;     // keys per workgroup (32 per wave)
+  constexpr int KC = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int QBN = BRQ / 32;   // 32-row query blocks per tile
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BRQ * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BRQ * CPR / NT;
+  static_assert((BRQ * CPR) % NT == 0 && BRQ <= NT, "tile must divide over the threads");
+
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // Q[2], dO[2]
+  __shared__ __attribute__((aligned(16))) float sL[2][BRQ];      // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][BRQ];      // D
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int n_kt = (N + BC - 1) / BC;
+  int w = blockIdx.x;
+  xcd_remap(w, a.BH * n_kt);
+  const int bh = w / n_kt;
+  const int kt = w - bh * n_kt;  // ascending: under a causal mask the first key tiles see most rows
+  const size_t base = (size_t)bh * N * D;
+  const bf16* __restrict__ Q = (const bf16*)a.q + base;
+  const bf16* __restrict__ K = (const bf16*)a.k + base;
+  const bf16* __restrict__ V = (const bf16*)a.v + base;
+  const bf16* __restrict__ dO = (const bf16*)a.dout + base;
+  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
+  const float* __restrict__ Dl = a.delta + (size_t)bh * N;
+  const int k0 = kt * BC;
+  const int kw0 = k0 + wv * 32;
+  const int key = kw0 + l32;  // this lane's key in the S / dP accumulators
+
+  bf16x8 kop[KC], vop[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < N) {
+      x = *(const u32x4*)(K + (size_t)key * D + kc * 16 + h * 8);
+      y = *(const u32x4*)(V + (size_t)key * D + kc * 16 + h * 8);
+    }
+    x = (x & a.q_and) ^ a.q_xor;  // sign / zero of the scale folded into K
+    kop[kc] = __builtin_bit_cast(bf16x8, x);
+    vop[kc] = __builtin_bit_cast(bf16x8, y);
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+  const float c = a.scale_log2;
+  const float LOG2E = 1.4426950408889634f;
+
+  // query rows that can see keys [k0, k0 + BC)
+  int q_lo = 0, q_hi = N;
+  if (MASK == MASK_CAUSAL) q_lo = k0;
+  if (MASK == MASK_LOCAL) {
+    q_lo = k0 - a.window > 0 ? k0 - a.window : 0;
+    const long long hh = (long long)k0 + BC + a.window;
+    q_hi = hh < N ? (int)hh : N;
+  }
+  const int t_begin = q_lo / BRQ, t_end = q_lo < q_hi ? (q_hi + BRQ - 1) / BRQ : t_begin;
+
+  u32x4 stQ[CPT], stO[CPT];
+  float stL = 0.f, stD = 0.f;
+  auto gload = [&](int t) {
+    const int r0 = t * BRQ;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int row = ch / CPR, cc = ch % CPR;
+      const int gr = r0 + row;
+      u32x4 zq = {0u, 0u, 0u, 0u}, zo = {0u, 0u, 0u, 0u};
+      if (gr < N) {
+        zq = *(const u32x4*)(Q + (size_t)gr * D + cc * 8);
+        zo = *(const u32x4*)(dO + (size_t)gr * D + cc * 8);
+      }
+      stQ[i] = zq;
+      stO[i] = zo;
+    }
+    if (tid < BRQ) {
+      const int gr = r0 + tid;
+      stL = gr < N ? LSE[gr] * LOG2E : INFINITY;  // padded rows get P = 0
+      stD = gr < N ? Dl[gr] : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+    char* sQ = smem + buf * TILEB;
+    char* sO = smem + (2 + buf) * TILEB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int row = ch / CPR, cc = ch % CPR;
+      const int off = row * ROWB + ((cc ^ swz_dual<D>(row)) << 4);
+      *(u32x4*)(sQ + off) = stQ[i];
+      *(u32x4*)(sO + off) = stO[i];
+    }
+    if (tid < BRQ) {
+      sL[buf][tid] = stL;
+      sD[buf][tid] = stD;
+    }
+  };
+
+  if (t_begin < t_end) {
+    gload(t_begin);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const char* sQ = smem + buf * TILEB;
+    const char* sO = smem + (2 + buf) * TILEB;
+    if (t + 1 < t_end) gload(t + 1);
+    const int q0 = t * BRQ;
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+      const int qr0 = q0 + qb * 32;
+      // S = Q K^T and dP = dO V^T: accumulator lane <-> key, 16 query rows
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const int arow = qb * 32 + l32;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int off = arow * ROWB + (((2 * kc + h) ^ swz_dual<D>(arow)) << 4);
+        const bf16x8 qa = *(const bf16x8*)(sQ + off);
+        const bf16x8 oa = *(const bf16x8*)(sO + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[kc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vop[kc], dp, 0, 0, 0);
+      }
+      const bool need_mask = !tile_full<MASK>(qr0, qr0 + 32, kw0, kw0 + 32, a.window);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 L4 = *(const f32x4*)&sL[buf][qb * 32 + 8 * rr + 4 * h];
+        const f32x4 D4 = *(const f32x4*)&sD[buf][qb * 32 + 8 * rr + 4 * h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float sv = s[r];
+          if (need_mask && !allowed<MASK>(qr0 + 8 * rr + 4 * h + e, key, a.window)) sv = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -L4[e]));
+          s[r] = p;
+          dp[r] = p * (dp[r] - D4[e]);
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q (A operands straight from registers)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pa, da;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pa[e] = (bf16)s[8 * u + e];
+          da[e] = (bf16)dp[8 * u + e];
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          i16x4 olo, ohi, qlo, qhi;
+          const int rlo = qb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rhi) << 1)) * 8;
+          olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sO + rlo * ROWB + clo));
+          ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sO + rhi * ROWB + chi));
+          qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sQ + rlo * ROWB + clo));
+          qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sQ + rhi * ROWB + chi));
+          const bf16x8 ob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 qbv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ob, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qbv, dk[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < t_end) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane holds value column dt*32 + l32 of keys kw0 + 8(r/4) + 4h + (r%4)
+  bf16* __restrict__ dK = (bf16*)a.dk + base;
+  bf16* __restrict__ dV = (bf16*)a.dv + base;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kr = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (kr < N) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dK[(size_t)kr * D + dt * 32 + l32] = (bf16)(dk[dt][r] * a.scale);
+        dV[(size_t)kr * D + dt * 32 + l32] = (bf16)dv[dt][r];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------- dQ
+template <int D, int NW, int BC, int MASK>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;
+  constexpr int KC = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KB = BC / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BC * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BC * CPR / NT;
+  static_assert((BC * CPR) % NT == 0, "tile chunks must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2] (dual), V[2]
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int n_qt = (N + BR - 1) / BR;
+  int w = blockIdx.x;
+  xcd_remap(w, a.BH * n_qt);
+  const int bh = w / n_qt;
+  int qt = w - bh * n_qt;
+  if (MASK == MASK_CAUSAL) qt = n_qt - 1 - qt;
+  const size_t base = (size_t)bh * N * D;
+  const bf16* __restrict__ Q = (const bf16*)a.q + base;
+  const bf16* __restrict__ K = (const bf16*)a.k + base;
+  const bf16* __restrict__ V = (const bf16*)a.v + base;
+  const bf16* __restrict__ dO = (const bf16*)a.dout + base;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wv * 32;
+  const int qi = qw0 + l32;  // this lane's query row
+
+  bf16x8 qop[KC], oop[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (qi < N) {
+      x = *(const u32x4*)(Q + (size_t)qi * D + kc * 16 + h * 8);
+      y = *(const u32x4*)(dO + (size_t)qi * D + kc * 16 + h * 8);
+    }
+    x = (x & a.q_and) ^ a.q_xor;
+    qop[kc] = __builtin_bit_cast(bf16x8, x);
+    oop[kc] = __builtin_bit_cast(bf16x8, y);
+  }
+  const float Lq = qi < N ? a.lse[(size_t)bh * N + qi] * 1.4426950408889634f : INFINITY;
+  const float Dq = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  const float c = a.scale_log2;
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  int k_lo, k_hi;
+  key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
+  const int t_begin = k_lo / BC, t_end = (k_hi + BC - 1) / BC;
+
+  u32x4 stK[CPT], stV[CPT];
+  auto gload = [&](int t) {
+    const int r0 = t * BC;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int row = ch / CPR, cc = ch % CPR;
+      const int gr = r0 + row;
+      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+      if (gr < N) {
+        zk = *(const u32x4*)(K + (size_t)gr * D + cc * 8);
+        zv = *(const u32x4*)(V + (size_t)gr * D + cc * 8);
+      }
+      stK[i] = zk;
+      stV[i] = zv;
+    }
+  };
+  auto lstore = [&](int buf) {
+    char* sK = smem + buf * TILEB;
+    char* sV = smem + (2 + buf) * TILEB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int row = ch / CPR, cc = ch % CPR;
+      const int off = row * ROWB + ((cc ^ swz_dual<D>(row)) << 4);
+      *(u32x4*)(sK + off) = stK[i];
+      *(u32x4*)(sV + off) = stV[i];
+    }
+  };
+  if (t_begin < t_end) {
+    gload(t_begin);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const char* sK = smem + buf * TILEB;
+    const char* sV = smem + (2 + buf) * TILEB;
+    if (t + 1 < t_end) gload(t + 1);
+    const int k0 = t * BC;
+    bf16x8 dsb[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const int arow = kb * 32 + l32;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int off = arow * ROWB + (((2 * kc + h) ^ swz_dual<D>(arow)) << 4);
+        const bf16x8 ka = *(const bf16x8*)(sK + off);
+        const bf16x8 va = *(const bf16x8*)(sV + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[kc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, oop[kc], dp, 0, 0, 0);
+      }
+      const int kb0 = k0 + kb * 32;
+      const bool need_mask =
+          (kb0 + 32 > N) || !tile_full<MASK>(qw0, qw0 + 32, kb0, kb0 + 32, a.window);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sv = s[r];
+        if (need_mask) {
+          const int kk = kb0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (!(kk < N && allowed<MASK>(qi, kk, a.window))) sv = -INFINITY;
+        }
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -Lq));
+        s[r] = p * (dp[r] - Dq);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsb[kb][u][e] = (bf16)s[8 * u + e];
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rhi) << 1)) * 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sK + rlo * ROWB + clo));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sK + rhi * ROWB + chi));
+          const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsb[kb][u], dq[dt], 0, 0, 0);
+        }
+    if (t + 1 < t_end) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qi < N) {
+    bf16* __restrict__ dQ = (bf16*)a.dq + base + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)(dq[dt][4 * r4 + e] * a.scale);
+        *(bf16x4*)(dQ + dt * 32 + 8 * r4 + 4 * h) = y;
+      }
+  }
+}
+
+// ------------------------------------------------------------ float32 path
+constexpr int F32B_T = 128;  // rows (keys or queries) per workgroup, one per thread
+constexpr int F32B_TILE = 32;
+
+__global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restrict__ o,
+                                                          const float* __restrict__ dout,
+                                                          float* __restrict__ delta, long rows,
+                                                          int d) {
+  const long row = (long)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  float acc = 0.f;
+  for (int c = 0; c < d; ++c) acc = fmaf(o[row * d + c], dout[row * d + c], acc);
+  delta[row] = acc;
+}
+
+template <int DP, int MASK>
+__global__ __launch_bounds__(F32B_T) void bwd_dkdv_f32_kernel(BwdArgs a) {
+  __shared__ float sQ[F32B_TILE][DP], sO[F32B_TILE][DP], sL[F32B_TILE], sDl[F32B_TILE];
+  const int N = a.N, d = a.d;
+  const int n_t = (N + F32B_T - 1) / F32B_T;
+  const int bh = blockIdx.x / n_t;
+  const int k0 = (blockIdx.x - bh * n_t) * F32B_T;
+  const int kj = k0 + (int)threadIdx.x;
+  const size_t base = (size_t)bh * N * d;
+  const float* Q = (const float*)a.q + base;
+  const float* K = (const float*)a.k + base;
+  const float* V = (const float*)a.v + base;
+  const float* dO = (const float*)a.dout + base;
+  float k[DP], v[DP], dk[DP], dv[DP];
+#pragma unroll
+  for (int cc = 0; cc < DP; ++cc) {
+    const bool ok = kj < N && cc < d;
+    k[cc] = ok ? K[(size_t)kj * d + cc] : 0.f;
+    v[cc] = ok ? V[(size_t)kj * d + cc] : 0.f;
+    dk[cc] = 0.f;
+    dv[cc] = 0.f;
+  }
+  int q_lo = 0, q_hi = N;
+  if (MASK == MASK_CAUSAL) q_lo = k0;
+  if (MASK == MASK_LOCAL) {
+    q_lo = k0 - a.window > 0 ? k0 - a.window : 0;
+    const long long hh = (long long)k0 + F32B_T + a.window;
+    q_hi = hh < N ? (int)hh : N;
+  }
+  for (int r0 = (q_lo / F32B_TILE) * F32B_TILE; r0 < q_hi; r0 += F32B_TILE) {
+    for (int idx = threadIdx.x; idx < F32B_TILE * DP; idx += F32B_T) {
+      const int r = idx / DP, cc = idx % DP, qi = r0 + r;
+      const bool ok = qi < N && cc < d;
+      sQ[r][cc] = ok ? Q[(size_t)qi * d + cc] : 0.f;
+      sO[r][cc] = ok ? dO[(size_t)qi * d + cc] : 0.f;
+    }
+    if (threadIdx.x < F32B_TILE) {
+      const int qi = r0 + threadIdx.x;
+      sL[threadIdx.x] = qi < N ? a.lse[(size_t)bh * N + qi] : 0.f;
+      sDl[threadIdx.x] = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < F32B_TILE; ++r) {
+      const int qi = r0 + r;
+      if (qi >= N || kj >= N || !allowed<MASK>(qi, kj, a.window)) continue;
+      float s = 0.f, dpv = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < DP; ++cc) {
+        s = fmaf(sQ[r][cc], k[cc], s);
+        dpv = fmaf(sO[r][cc], v[cc], dpv);
+      }
+      const float p = expf(a.scale * s - sL[r]);
+      const float ds = p * (dpv - sDl[r]);
+#pragma unroll
+      for (int cc = 0; cc < DP; ++cc) {
+        dv[cc] = fmaf(p, sO[r][cc], dv[cc]);
+        dk[cc] = fmaf(ds, sQ[r][cc], dk[cc]);
+      }
+    }
+    __syncthreads();
+  }
+  if (kj < N) {
+    for (int cc = 0; cc < d && cc < DP; ++cc) {
+      ((float*)a.dk)[base + (size_t)kj * d + cc] = a.scale * dk[cc];
+      ((float*)a.dv)[base + (size_t)kj * d + cc] = dv[cc];
+    }
+  }
+}
+
+template <int DP, int MASK>
+__global__ __launch_bounds__(F32B_T) void bwd_dq_f32_kernel(BwdArgs a) {
+  __shared__ float sK[F32B_TILE][DP], sV[F32B_TILE][DP];
+  const int N = a.N, d = a.d;
+  const int n_t = (N + F32B_T - 1) / F32B_T;
+  const int bh = blockIdx.x / n_t;
+  const int q0 = (blockIdx.x - bh * n_t) * F32B_T;
+  const int qi = q0 + (int)threadIdx.x;
+  const size_t base = (size_t)bh * N * d;
+  const float* Q = (const float*)a.q + base;
+  const float* K = (const float*)a.k + base;
+  const float* V = (const float*)a.v + base;
+  const float* dO = (const float*)a.dout + base;
+  float q[DP], o[DP], dq[DP];
+#pragma unroll
+  for (int cc = 0; cc < DP; ++cc) {
+    const bool ok = qi < N && cc < d;
+    q[cc] = ok ? Q[(size_t)qi * d + cc] : 0.f;
+    o[cc] = ok ? dO[(size_t)qi * d + cc] : 0.f;
+    dq[cc] = 0.f;
+  }
+  const float L = qi < N ? a.lse[(size_t)bh * N + qi] : 0.f;
+  const float Dv = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  int k_lo, k_hi;
+  key_range<MASK>(q0, q0 + F32B_T, N, a.window, k_lo, k_hi);
+  for (int r0 = (k_lo / F32B_TILE) * F32B_TILE; r0 < k_hi; r0 += F32B_TILE) {
+    for (int idx = threadIdx.x; idx < F32B_TILE * DP; idx += F32B_T) {
+      const int r = idx / DP, cc = idx % DP, kj = r0 + r;
+      const bool ok = kj < N && cc < d;
+      sK[r][cc] = ok ? K[(size_t)kj * d + cc] : 0.f;
+      sV[r][cc] = ok ? V[(size_t)kj * d + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < F32B_TILE; ++r) {
+      const int kj = r0 + r;
+      if (qi >= N || kj >= N || !allowed<MASK>(qi, kj, a.window)) continue;
+      float s = 0.f, dpv = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < DP; ++cc) {
+        s = fmaf(q[cc], sK[r][cc], s);
+        dpv = fmaf(o[cc], sV[r][cc], dpv);
+      }
+      const float p = expf(a.scale * s - L);
+      const float ds = p * (dpv - Dv);
+#pragma unroll
+      for (int cc = 0; cc < DP; ++cc) dq[cc] = fmaf(ds, sK[r][cc], dq[cc]);
+    }
+    __syncthreads();
+  }
+  if (qi < N)
+    for (int cc = 0; cc < d && cc < DP; ++cc)
+      ((float*)a.dq)[base + (size_t)qi * d + cc] = a.scale * dq[cc];
+}
+
+// ------------------------------------------------------------------ launch
+template <int D, int MASK>
+static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, hipStream_t stream) {
+  constexpr int KV_NW = 4, KV_BRQ = 64;   // 128 keys per dK/dV workgroup
+  constexpr int Q_NW = 8, Q_BC = 64;      // 256 query rows per dQ workgroup
+  const long rows = (long)a.BH * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                     0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_kt = (a.N + KV_NW * 32 - 1) / (KV_NW * 32);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, KV_NW, KV_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
+                     dim3(KV_NW * 64), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qt = (a.N + Q_NW * 32 - 1) / (Q_NW * 32);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, Q_NW, Q_BC, MASK>), dim3((unsigned)(n_qt * a.BH)),
+                     dim3(Q_NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DP, int MASK>
+static hipError_t launch_bwd_f32_mask(const BwdArgs& a, hipStream_t stream) {
+  const long rows = (long)a.BH * a.N;
+  hipLaunchKernelGGL(bwd_pre_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)a.o, (const float*)a.dout, a.delta, rows, a.d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_t = (a.N + F32B_T - 1) / F32B_T;
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DP, MASK>), dim3((unsigned)(n_t * a.BH)), dim3(F32B_T), 0,
+                     stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<DP, MASK>), dim3((unsigned)(n_t * a.BH)), dim3(F32B_T), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int MASK>
+static hipError_t launch_bwd_mask(const BwdArgs& a, int bf16_path, hipStream_t stream) {
+  if (bf16_path) {
+    if (a.d == 128) return launch_bwd_bf16_mask<128, MASK>(a, stream);
+    return launch_bwd_bf16_mask<64, MASK>(a, stream);
+  }
+  if (a.d <= 8) return launch_bwd_f32_mask<8, MASK>(a, stream);
+  if (a.d <= 32) return launch_bwd_f32_mask<32, MASK>(a, stream);
+  if (a.d <= 64) return launch_bwd_f32_mask<64, MASK>(a, stream);
+  return launch_bwd_f32_mask<128, MASK>(a, stream);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int bf16_path, int mask, hipStream_t stream) {
+  switch (mask) {
+    case MASK_CAUSAL: return launch_bwd_mask<MASK_CAUSAL>(a, bf16_path, stream);
+    case MASK_LOCAL: return launch_bwd_mask<MASK_LOCAL>(a, bf16_path, stream);
+    default: return launch_bwd_mask<MASK_NONE>(a, bf16_path, stream);
+  }
+}
+
+}  // namespace fa

@@ -9,15 +9,8 @@ namespace fa {
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t bwd_workspace_bytes(int BH, int N, int d) {
-  return round256((size_t)BH * N * d * sizeof(float)) + round256((size_t)BH * N * sizeof(float));
-}
-
-void bwd_workspace_split(void* ws, int BH, int N, int d, float** dq_acc, float** delta) {
-  char* p = (char*)ws;
-  *dq_acc = (float*)p;
-  *delta = (float*)(p + round256((size_t)BH * N * d * sizeof(float)));
-}
+// The workspace holds D_i = <dO_i, O_i> for every row, float32 [BH][N].
+size_t bwd_workspace_bytes(int BH, int N) { return round256((size_t)BH * N * sizeof(float)); }
 
 }  // namespace fa
 
@@ -46,7 +39,7 @@ extern "C" {
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
   if (check_problem(B, H, N, d, dtype) != FA_OK) return 0;
-  return fa::bwd_workspace_bytes(B * H, N, d);
+  return fa::bwd_workspace_bytes(B * H, N);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -62,7 +55,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  const size_t need = fa::bwd_workspace_bytes(B * H, N);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   const size_t tb = (size_t)B * H * N * d * (dtype == FA_BF16 ? 2 : 4);
   const size_t lb = (size_t)B * H * N * sizeof(float);
@@ -82,7 +75,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  fa::bwd_workspace_split(workspace, B * H, N, d, &a.dq_acc, &a.delta);
+  a.delta = (float*)workspace;
   a.BH = B * H;
   a.N = N;
   a.d = d;

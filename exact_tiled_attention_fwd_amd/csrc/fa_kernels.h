@@ -52,7 +52,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;   // workspace: [BH][N][d] float32 dQ accumulator
   float* delta;    // workspace: [BH][N] float32, D_i = <dO_i, O_i>
   int BH;
   int N;
@@ -66,8 +65,7 @@ struct BwdArgs {
 };
 
 // Workspace layout shared by fa_bwd_workspace_bytes and the launcher.
-size_t bwd_workspace_bytes(int BH, int N, int d);
-void bwd_workspace_split(void* ws, int BH, int N, int d, float** dq_acc, float** delta);
+size_t bwd_workspace_bytes(int BH, int N);
 
 hipError_t launch_bwd(const BwdArgs& a, int bf16, int mask, hipStream_t stream);
 

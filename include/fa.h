@@ -76,8 +76,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, fa_mask mask, int window, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this problem (a float32
- * row-statistics buffer and a float32 dQ accumulator). Returns 0 for an
+ * Bytes of device workspace fa_bwd needs for this problem: one float32 per
+ * query row (D_i = <dO_i, O_i>), rounded up to 256 bytes. Returns 0 for an
  * invalid problem description.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype);

@@ -1,0 +1,82 @@
+"""The C-ABI library loads and exports every entry point include/fa.h
+declares, and argument errors come back as status codes before any GPU work
+(CPU only: these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_fwd_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                             r"([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return _native.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"libfa.so does not export {n}"
+
+
+def test_status_strings(lib):
+    for code, name in _native.STATUS_NAMES.items():
+        assert _native.fa_status_string(code).startswith(name)
+    assert "unknown" in _native.fa_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+
+
+def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=ctypes.c_void_p(0x200000), lse=ctypes.c_void_p(0x900000),
+        B=1, H=1, N=8, d=64, dtype=1, scale=0.125, mask=0, window=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, mask, window, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert fwd(lib, q=None) == 1                      # FA_ERR_NULL
+    assert fwd(lib, N=0) == 2 and fwd(lib, B=-1) == 2  # FA_ERR_SHAPE
+    assert fwd(lib, dtype=7) == 3                     # FA_ERR_DTYPE
+    assert fwd(lib, d=96) == 4 and fwd(lib, d=32) == 4  # bf16 needs d in {64, 128}
+    assert fwd(lib, dtype=0, d=129) == 4 and fwd(lib, dtype=0, d=0) == 4
+    assert fwd(lib, mask=3) == 5 and fwd(lib, mask=2, window=-1) == 5
+    assert fwd(lib, scale=float("inf")) == 6 and fwd(lib, scale=float("nan")) == 6
+    assert fwd(lib, q=ctypes.c_void_p(0x100004)) == 7  # FA_ERR_ALIGN
+    assert fwd(lib, o=FAKE) == 10                     # output aliases an input
+    assert fwd(lib, N=1 << 30, d=128) == 2           # N * d beyond 2^31 - 1
+
+
+def test_bwd_argument_errors(lib):
+    ws_need = lib.fa_bwd_workspace_bytes(2, 3, 100, 64, 1)
+    assert ws_need >= 2 * 3 * 100 * 4 and ws_need % 256 == 0
+    assert lib.fa_bwd_workspace_bytes(0, 3, 100, 64, 1) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 100, 96, 1) == 0
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+
+    def bwd(ws=p[9], wsb=ws_need, scale=0.1, mask=0, window=0, d=64, q=p[0]):
+        return lib.fa_bwd(q, p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], ws, wsb,
+                          2, 3, 100, d, 1, scale, mask, window, None)
+    assert bwd(q=None) == 1
+    assert bwd(ws=None) == 8 and bwd(wsb=ws_need - 1) == 8
+    assert bwd(mask=2, window=-2) == 5
+    assert bwd(scale=float("nan")) == 6
+    assert bwd(d=100) == 4
