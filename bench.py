@@ -72,6 +72,11 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-headline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time fa_fwd alone on the workload (profiling aid)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB "
+                         "(calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
@@ -88,7 +93,11 @@ def main():
     fa.load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda", 0)
 
-    have_bwd = True
+    if args.copy_probe_mib:
+        copy_probe(torch, dev, args)
+        return
+
+    have_bwd = not args.fwd_only
     name = args.workload or "bf16_causal_bwd_b2h16_n4096_d128"
     w = WORKLOADS[name]
     inp = make_inputs(w, with_dout=True)
@@ -193,6 +202,29 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inp, have_bwd)
 
     print(json.dumps(out), flush=True)
+
+
+def copy_probe(torch, dev, args):
+    """A plain device-to-device copy of known size: its FETCH_SIZE and
+    WRITE_SIZE counters give the factor that turns counter readings into
+    bytes."""
+    n = args.copy_probe_mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "launches": args.steps + args.warmup, "avg_ms": round(ms, 4),
+                      "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, inp, have_bwd):
