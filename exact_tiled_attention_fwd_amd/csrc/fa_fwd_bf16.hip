@@ -26,6 +26,11 @@
 //    are bank-conflict free; the next tile's global loads are in flight
 //    while the current one is computed.
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
+//  * The subtracted maximum is refreshed lazily: the reference m only moves
+//    when some row's tile maximum exceeds it by more than 2^RESCALE_LOG2 in
+//    exp2 units, so most tiles skip the rescale of the accumulator (p then
+//    stays below 2^RESCALE_LOG2, harmless in float32 and bf16). Numerator
+//    and denominator share the reference, so the result is unchanged.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -45,10 +50,63 @@ __device__ __forceinline__ int swz_v16(int row) {
   else return ((row >> 1) & 1) << 2;
 }
 
+
+// Rescale threshold, in exp2 units, for the lazily refreshed maximum.
+constexpr float RESCALE_LOG2 = 8.0f;
+
+// v_permlane32_swap(a, b) exchanges the upper 32 lanes of a with the lower
+// 32 lanes of b. With b = a it returns {a of lanes 0..31 in both halves,
+// a of lanes 32..63 in both halves}, so a symmetric operation over the two
+// results gives lanes l and l^32 the same, bit-identical value. (The two
+// results are copied to plain scalars before reinterpretation: applying
+// __builtin_bit_cast to an element of the returned vector directly has been
+// seen to read element 0 twice.)
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  const unsigned u = __float_as_uint(x);
+  auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a0 = sw[0];
+  const unsigned a1 = sw[1];
+  lo = __uint_as_float(a0);
+  hi = __uint_as_float(a1);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  const float t0 = fmaxf(fmaxf(v[0], v[1]), v[2]);
+  const float t1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float t2 = fmaxf(fmaxf(v[6], v[7]), v[8]);
+  const float t3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float t4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), v[15]));
+}
+
+// Pairwise (depth-4) float32 sum of 16 accumulator values.
+__device__ __forceinline__ float sum16(const f32x16& v) {
+  const float a0 = (v[0] + v[1]) + (v[2] + v[3]);
+  const float a1 = (v[4] + v[5]) + (v[6] + v[7]);
+  const float a2 = (v[8] + v[9]) + (v[10] + v[11]);
+  const float a3 = (v[12] + v[13]) + (v[14] + v[15]);
+  return (a0 + a1) + (a2 + a3);
+}
+
+// Offset of accumulator register r within a 32-key block, for the lanes of
+// the lower half (the upper half adds 4): key = 8 (r / 4) + (r % 4).
+__device__ __forceinline__ constexpr int acc_key(int r) { return 8 * (r >> 2) + (r & 3); }
+
 template <int D, int QB, int NW, int BC, int MASK>
-__global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int BR = NW * QB * 32;  // query rows per workgroup
+  constexpr int QW = QB * 32;       // query rows per wave
+  constexpr int BR = NW * QW;       // query rows per workgroup
   constexpr int KC = D / 16;        // 16-wide chunks of the QK^T contraction
   constexpr int DT = D / 32;        // 32-column tiles of O^T
   constexpr int KB = BC / 32;       // 32-key blocks per K/V tile
@@ -59,7 +117,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   static_assert((BC * CPR) % NT == 0, "tile chunks must divide evenly");
   static_assert(BC % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2], V[2]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,9 +142,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   const bf16* __restrict__ K = a.k + base;
   const bf16* __restrict__ V = a.v + base;
   const int q0 = qt * BR;
-  const int qw0 = q0 + wv * QB * 32;  // first query row of this wave
+  const int qw0 = q0 + wv * QW;  // first query row of this wave
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[row][16kc + 8h .. +7].
+  // Q as the B operand of S^T = K Q^T: lane holds Q[row][16kc + 8h .. +7]
+  // for row = qw0 + 32 qb + l32.
   bf16x8 qop[QB][KC];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -107,18 +166,22 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
-  float m_run[QB], l_run[QB];
+  float m_ref[QB], l_run[QB];  // reference maximum (raw units), lane's part of l
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
+    m_ref[qb] = -INFINITY;
     l_run[qb] = 0.f;
   }
   const float c = a.scale_log2;  // > 0
 
+  // key tiles of the workgroup, and the contiguous sub-range this wave needs
   int k_lo, k_hi;
   key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
   const int t_begin = k_lo / BC;
   const int t_end = (k_hi + BC - 1) / BC;
+  int wk_lo, wk_hi;
+  key_range<MASK>(qw0, qw0 + QW, N, a.window, wk_lo, wk_hi);
+  const bool wave_live = qw0 < N;
 
   u32x4 stK[CPT], stV[CPT];
   auto gload = [&](int t) {
@@ -156,11 +219,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   __syncthreads();
 
   // Per-lane constants of the transposed V read: within each 16-lane group,
-  // lane s points at row 4*(s/4)+... of a 4-key x 16-column block.
-  const int g16 = lane >> 4;      // 16-lane group 0..3
+  // lane s addresses row 4h + s/4 and 8-byte chunk 4*(group&1) + s%4.
+  const int g16 = lane >> 4;
   const int s16 = lane & 15;
-  const int tr_row = 4 * h + (s16 >> 2);               // + 32kb + 16u + 8t
-  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);        // + 8dt  (8-byte chunks)
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
 
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = (t - t_begin) & 1;
@@ -169,117 +232,144 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 < t_end) gload(t + 1);
     const int k0 = t * BC;
 
-    // ---- S^T = K Q^T for BC keys x 32*QB queries
-    f32x16 sacc[QB][KB];
+    // Skip tiles that hold no allowed key for any row of this wave.
+    if (wave_live && k0 < wk_hi && k0 + BC > wk_lo) {
+      // ---- S^T = K Q^T for BC keys x QW queries; each K read feeds QB MFMAs
+      f32x16 sacc[QB][KB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int row = kb * 32 + l32;
-        const bf16x8 ka =
-            *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][kc], sacc[qb][kb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask (only where the tile is not fully visible to this wave)
-    const bool need_mask =
-        (k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + QB * 32, k0, k0 + BC, a.window);
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw0 + qb * 32 + l32;
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (!(key < N && allowed<MASK>(qi, key, a.window))) sacc[qb][kb][r] = -INFINITY;
-          }
-      }
-    }
-
-    // ---- online softmax update (per lane: one query, 16 keys per block)
-    bf16x8 pop[QB][KB][2];
+          for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+          const int row = kb * 32 + l32;
+          const bf16x8 ka =
+              *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float mc = m_use * c;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] * c - mc);
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][r], c, -mc));
-          sacc[qb][kb][r] = p;
-          ls += p;
+          for (int qb = 0; qb < QB; ++qb)
+            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][kc], sacc[qb][kb], 0, 0, 0);
         }
-      l_run[qb] = alpha * l_run[qb] + ls;
-      m_run[qb] = m_new;
+
+      // ---- mask, only where the tile is not fully visible to this wave
+      if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + QW, k0, k0 + BC, a.window)) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int qb = 0; qb < QB; ++qb) {
+          // key allowed iff lo_rel <= 32 kb + acc_key(r) <= hi_rel
+          const int qi = qw0 + qb * 32 + l32;
+          const int q_hi_key = MASK == MASK_CAUSAL ? min(qi, N - 1)
+                               : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
+          const int hi_rel = q_hi_key - k0 - 4 * h;
+          const int lo_rel = (MASK == MASK_LOCAL ? qi - a.window : 0) - k0 - 4 * h;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+            for (int r = 0; r < 16; ++r) {
+              const int kr = kb * 32 + acc_key(r);
+              const bool ok =
+                  (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
+              sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
+            }
+        }
+      }
+
+      // ---- online softmax (one query per lane and query block)
+      float mc[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = max16(sacc[qb][0]);
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, max16(sacc[qb][kb]));
+        mx = pair_max(mx);
+        // refresh the reference only when a row's maximum outgrew it
+        if (__builtin_amdgcn_ballot_w64((mx - m_ref[qb]) * c > RESCALE_LOG2)) {
+          const float m_new = fmaxf(m_ref[qb], mx);
+          // 0 when the row had no key before; 1 while it still has none
+          const float alpha =
+              m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref[qb] - m_new) * c);
+          m_ref[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+        }
+        mc[qb] = (m_ref[qb] == -INFINITY ? 0.f : m_ref[qb]) * c;
+      }
+      bf16x8 pop[QB][KB][2];
+      float ls[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ls[qb] = 0.f;
+      // exp of one 32-key block (all query blocks), its row-sum part and its
+      // bf16 MFMA operand
+      auto exp_block = [&](int kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[qb][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][r], c, -mc[qb]));
+          ls[qb] += sum16(sacc[qb][kb]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pop[qb][kb][u][e] = (bf16)sacc[qb][kb][8 * u + e];
+        }
+      };
+      // O^T += V^T P^T for one 32-key block; each V read feeds QB MFMAs
+      auto pv_block = [&](int kb) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int s = 0; s < 8; ++s) pop[qb][kb][u][s] = (bf16)sacc[qb][kb][8 * u + s];
-    }
-
-    // ---- O^T += V^T P^T
+          for (int dt = 0; dt < DT; ++dt) {
+            const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+            const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+            const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
+            const bf16x8 va = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          i16x4 lo, hi;
-          {
-            const int row = kb * 32 + 16 * u + tr_row;
-            const int ch = (dt * 8 + tr_ch8) ^ (swz_v16<D>(row) << 1);
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + row * ROWB + ch * 8));
+            for (int qb = 0; qb < QB; ++qb)
+              oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][kb][u], oacc[qb][dt], 0, 0, 0);
           }
-          {
-            const int row = kb * 32 + 16 * u + 8 + tr_row;
-            const int ch = (dt * 8 + tr_ch8) ^ (swz_v16<D>(row) << 1);
-            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + row * ROWB + ch * 8));
-          }
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      // Software pipeline over the key blocks: the PV MFMAs of block kb-1
+      // share a scheduling region with the exp / convert VALU work of block
+      // kb, interleaved a few VALU ops per MFMA, so the matrix core and the
+      // vector ALU of the wave run concurrently.
+      exp_block(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][kb][u], oacc[qb][dt], 0, 0, 0);
+      for (int kb = 1; kb < KB; ++kb) {
+        pv_block(kb - 1);
+        exp_block(kb);
+#pragma unroll
+        for (int i = 0; i < 2 * DT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // 2 LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // QB MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x002, 28 * QB / DT, 0);  // VALU
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pv_block(KB - 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb];
+    }
 
     if (t + 1 < t_end) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l, LSE = m*scale + ln l
+  // ---- epilogue: O = acc / l, LSE = m * scale + ln l
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const float inv = 1.f / lt;
+    const float lt = pair_sum(l_run[qb]);
     const int qi = qw0 + qb * 32 + l32;
     if (qi < N) {
+      const float inv = 1.f / lt;
       bf16* O = a.o + base + (size_t)qi * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -290,9 +380,273 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
           for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[qb][dt][4 * r4 + e] * inv);
           *(bf16x4*)(O + dt * 32 + 8 * r4 + 4 * h) = y;
         }
-      if (h == 0) a.lse[(size_t)bh * N + qi] = m_run[qb] * a.scale_abs + logf(lt);
+      if (h == 0) a.lse[(size_t)bh * N + qi] = m_ref[qb] * a.scale_abs + logf(lt);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong schedule. The eight waves form two groups of four, one wave of
+// each group per SIMD. Every wave alternates an MFMA phase (scores of tile j
+// and P V of tile j-1) and a VALU phase (online softmax of tile j), and the
+// two groups run one phase apart, separated by workgroup barriers: while one
+// group keeps the matrix core busy, the other group's exp / max / convert
+// work runs on the vector ALU of the same SIMD.
+//
+// Global phase f: group 0 is in MFMA phase f/2 when f is even, group 1 when
+// f is odd. K_j is read in phases 2j, 2j+1 and V_j in 2j+2, 2j+3, so both
+// are double-buffered, and odd phase 2i+1 stores K_{i+1} and V_i to LDS
+// (their buffers were last read in phase 2i-1).
+template <int D, int BC, int MASK>
+__global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;
+  constexpr int KC = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KB = BC / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BC * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BC * CPR / NT;
+  static_assert((BC * CPR) % NT == 0, "tile chunks must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2], V[2]
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int grp = wv >> 2;  // waves w and w+4 share a SIMD
+  const int N = a.N;
+
+  const int total = a.BH * a.n_qtiles;
+  int w = blockIdx.x;
+  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
+  const int bh = w / a.n_qtiles;
+  int qt = w - bh * a.n_qtiles;
+  if (MASK == MASK_CAUSAL) qt = a.n_qtiles - 1 - qt;
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const bf16* __restrict__ Q = a.q + base;
+  const bf16* __restrict__ K = a.k + base;
+  const bf16* __restrict__ V = a.v + base;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wv * 32;
+  const int qi = qw0 + l32;
+
+  bf16x8 qop[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < N) x = *(const u32x4*)(Q + (size_t)qi * D + kc * 16 + h * 8);
+    x = (x & a.q_and) ^ a.q_xor;
+    qop[kc] = __builtin_bit_cast(bf16x8, x);
+  }
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  int k_lo, k_hi;
+  key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
+  const int tb = k_lo / BC;
+  const int T = (k_hi + BC - 1) / BC - tb;  // tiles of this workgroup (>= 1)
+  int wk_lo, wk_hi;
+  key_range<MASK>(qw0, qw0 + 32, N, a.window, wk_lo, wk_hi);
+  const bool wave_live = qw0 < N;
+  auto active = [&](int j) {  // tile j (relative) holds allowed keys for this wave
+    const int k0 = (tb + j) * BC;
+    return wave_live && j >= 0 && j < T && k0 < wk_hi && k0 + BC > wk_lo;
+  };
+  const int q_hi_key = MASK == MASK_CAUSAL ? min(qi, N - 1)
+                       : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
+  const int q_lo_key = MASK == MASK_LOCAL ? qi - a.window : 0;
+
+  // staging of K_{i+1} and V_i (global -> registers -> LDS)
+  u32x4 stK[CPT], stV[CPT];
+  auto gload_k = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int gr = (tb + j) * BC + ch / CPR;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (j < T && gr < N) z = *(const u32x4*)(K + (size_t)gr * D + (ch % CPR) * 8);
+      stK[i] = z;
+    }
+  };
+  auto gload_v = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int gr = (tb + j) * BC + ch / CPR;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (j < T && gr < N) z = *(const u32x4*)(V + (size_t)gr * D + (ch % CPR) * 8);
+      stV[i] = z;
+    }
+  };
+  auto lstore_k = [&](int j) {
+    char* sK = smem + (j & 1) * TILEB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int row = ch / CPR, cc = ch % CPR;
+      *(u32x4*)(sK + row * ROWB + ((cc ^ swz_k16<D>(row)) << 4)) = stK[i];
+    }
+  };
+  auto lstore_v = [&](int j) {
+    char* sV = smem + (2 + (j & 1)) * TILEB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + NT * i;
+      const int row = ch / CPR, cc = ch % CPR;
+      *(u32x4*)(sV + row * ROWB + ((cc ^ swz_v16<D>(row)) << 4)) = stV[i];
+    }
+  };
+
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+
+  f32x16 sacc[KB];
+  bf16x8 pop[KB][2];
+
+  auto qk = [&](int j) {
+    const char* sK = smem + (j & 1) * TILEB;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row = kb * 32 + l32;
+        const bf16x8 ka =
+            *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[kc], sacc[kb], 0, 0, 0);
+      }
+  };
+  auto pv = [&](int j) {
+    const char* sV = smem + (2 + (j & 1)) * TILEB;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[kb][u], oacc[dt], 0, 0, 0);
+        }
+  };
+  auto softmax = [&](int j) {
+    const int k0 = (tb + j) * BC;
+    if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + 32, k0, k0 + BC, a.window)) {
+      const int hi_rel = q_hi_key - k0 - 4 * h;
+      const int lo_rel = q_lo_key - k0 - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kb * 32 + acc_key(r);
+          const bool ok = (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
+          sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+        }
+    }
+    float mx = max16(sacc[0]);
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, max16(sacc[kb]));
+    mx = pair_max(mx);
+    if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > RESCALE_LOG2)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * c;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
+      ls += sum16(sacc[kb]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pop[kb][u][e] = (bf16)sacc[kb][8 * u + e];
+    }
+    l_run += ls;
+  };
+
+  // prologue: K_0 resident; K_1, V_0 in flight
+  gload_k(0);
+  lstore_k(0);
+  gload_k(1);
+  gload_v(0);
+  __syncthreads();
+
+  for (int f = 0; f < 2 * T + 2; ++f) {
+    const bool mfma_phase = ((f & 1) == grp);
+    const int j = (f - grp) >> 1;  // this wave's step (MFMA phase j, or VALU phase j-?)
+    if (mfma_phase) {
+      // MFMA phase j: scores of tile j, P V of tile j-1
+      if (active(j)) qk(j);
+      if (active(j - 1)) pv(j - 1);
+    } else {
+      // VALU phase: softmax of the tile whose scores the last MFMA phase made
+      const int js = grp == 0 ? (f - 1) >> 1 : (f >> 1) - 1;
+      if (active(js)) softmax(js);
+    }
+    if (f & 1) {
+      // odd phase 2i+1: store K_{i+1} and V_i, start loading K_{i+2}, V_{i+1}
+      const int i = f >> 1;
+      lstore_k(i + 1);
+      lstore_v(i);
+      gload_k(i + 2);
+      gload_v(i + 1);
+    }
+    __syncthreads();
+  }
+
+  const float lt = pair_sum(l_run);
+  if (qi < N) {
+    const float inv = 1.f / lt;
+    bf16* O = a.o + base + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[dt][4 * r4 + e] * inv);
+        *(bf16x4*)(O + dt * 32 + 8 * r4 + 4 * h) = y;
+      }
+    if (h == 0) a.lse[(size_t)bh * N + qi] = m_ref * a.scale_abs + logf(lt);
+  }
+}
+
+template <int D, int BC>
+static hipError_t launch_fwd_bf16_pp(const FwdArgs& a0, int mask, hipStream_t stream) {
+  FwdArgs a = a0;
+  a.n_qtiles = (a.N + 255) / 256;
+  dim3 grid((unsigned)(a.n_qtiles * a.BH)), block(512);
+  switch (mask) {
+    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
+    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, BC, MASK_NONE>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
 }
 
 template <int D, int QB, int NW, int BC>
@@ -309,23 +663,26 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
   return hipGetLastError();
 }
 
-// Tile configurations (QB x 32 query rows per wave, NW waves, BC keys per
-// tile). The default was picked by measurement on MI355X: one 32-row query
-// block per wave and eight waves (two per SIMD) beat the register-heavy
-// two-block waves, which leave no second wave to overlap softmax with MFMA.
+// Tile configurations (NW waves of QB x 32 query rows, BC keys per tile).
+// The default was picked by measurement on MI355X; the others stay
+// selectable for tuning sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
     switch (cfg) {
-      case 1: return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
-      case 2: return launch_fwd_bf16_cfg<128, 2, 4, 32>(a, mask, stream);
-      case 4: return launch_fwd_bf16_cfg<128, 2, 4, 64>(a, mask, stream);
-      default: return launch_fwd_bf16_cfg<128, 1, 8, 64>(a, mask, stream);
+      case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64>(a, mask, stream);
+      case 2: return launch_fwd_bf16_cfg<128, 2, 4, 64>(a, mask, stream);
+      case 3: return launch_fwd_bf16_cfg<128, 2, 4, 32>(a, mask, stream);
+      case 4: return launch_fwd_bf16_pp<128, 64>(a, mask, stream);
+      case 5: return launch_fwd_bf16_pp<128, 32>(a, mask, stream);
+      default: return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
     }
   }
   switch (cfg) {
-    case 1: return launch_fwd_bf16_cfg<64, 1, 4, 64>(a, mask, stream);
-    case 2: return launch_fwd_bf16_cfg<64, 2, 4, 32>(a, mask, stream);
-    case 4: return launch_fwd_bf16_cfg<64, 2, 4, 64>(a, mask, stream);
+    case 1: return launch_fwd_bf16_cfg<64, 1, 8, 128>(a, mask, stream);
+    case 2: return launch_fwd_bf16_cfg<64, 2, 4, 64>(a, mask, stream);
+    case 3: return launch_fwd_bf16_cfg<64, 2, 4, 128>(a, mask, stream);
+    case 4: return launch_fwd_bf16_pp<64, 64>(a, mask, stream);
+    case 5: return launch_fwd_bf16_pp<64, 128>(a, mask, stream);
     default: return launch_fwd_bf16_cfg<64, 1, 8, 64>(a, mask, stream);
   }
 }
