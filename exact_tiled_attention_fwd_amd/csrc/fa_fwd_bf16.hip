@@ -102,7 +102,23 @@ __device__ __forceinline__ float sum16(const f32x16& v) {
 // the lower half (the upper half adds 4): key = 8 (r / 4) + (r % 4).
 __device__ __forceinline__ constexpr int acc_key(int r) { return 8 * (r >> 2) + (r & 3); }
 
-template <int D, int QB, int NW, int BC, int MASK>
+// Swizzle of the transposed V tile (rows = value columns, BC keys per row):
+// 16-byte chunk c of row r sits at chunk c ^ swz_vt(r). Conflict free (or
+// 2-way at 64-key rows) both for the 16-byte operand reads (32 consecutive
+// rows, one chunk) and for the staging writes (16 rows eight apart).
+template <int BC>
+__device__ __forceinline__ int swz_vt(int row) {
+  if constexpr (BC == 128) return (row ^ (row >> 4)) & 15;
+  else return ((row >> 1) ^ (row >> 4)) & 7;
+}
+
+// Key-row permutation of the QK^T A operand used with the transposed V
+// tile: swapping bits 2 and 3 of the row makes accumulator register r of a
+// lane hold key 16 (r / 8) + 8 h + r % 8, so each lane's 8 probabilities of
+// a 16-key PV step are consecutive keys.
+__device__ __forceinline__ int perm_rows(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+template <int D, int QB, int NW, int BC, int MASK, bool DMA, bool VT = false>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QW = QB * 32;       // query rows per wave
@@ -183,11 +199,71 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   key_range<MASK>(qw0, qw0 + QW, N, a.window, wk_lo, wk_hi);
   const bool wave_live = qw0 < N;
 
-  u32x4 stK[CPT], stV[CPT];
+  // K/V staging. Register path: global -> VGPR -> LDS. DMA path:
+  // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS at the wave's
+  // base + 16 i, so each lane fetches the global chunk that belongs at its
+  // LDS slot under the XOR swizzle. Rows past N are clamped to row N-1:
+  // their keys are masked, so only finiteness of the data matters.
+  constexpr int CPW = DMA ? CPT : 1;  // 16-byte chunks per lane per tile (DMA)
+  u32x4 stK[DMA ? 1 : CPT], stV[DMA ? 1 : CPT];
+  auto dma = [&](int t, int buf) {
+    const int k0 = t * BC;
+    char* sK = smem + buf * TILEB;
+    char* sV = smem + (2 + buf) * TILEB;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int slot = (wv * CPW + j) * 64;  // first LDS chunk of this instruction
+      const int p = slot + lane;
+      const int row = p / CPR;
+      int gr = k0 + row;
+      gr = gr < N ? gr : N - 1;
+      const int ck = (p % CPR) ^ swz_k16<D>(row);
+      __builtin_amdgcn_global_load_lds(K + (size_t)gr * D + ck * 8, (FA_LDS void*)(sK + slot * 16), 16, 0, 0);
+      if constexpr (!VT) {
+        const int cv = (p % CPR) ^ swz_v16<D>(row);
+        __builtin_amdgcn_global_load_lds(V + (size_t)gr * D + cv * 8, (FA_LDS void*)(sV + slot * 16), 16, 0, 0);
+      }
+    }
+  };
+  // Transposed V staging: thread (kg, cc) loads keys KPT*kg .. +KPT-1 of the
+  // 8 value columns 8cc .. 8cc+7 (rows past N read as zero), and writes, for
+  // each of those columns, its KPT keys into row 8cc+i of the V^T tile.
+  constexpr int KPT = VT ? BC * CPR / NT : 1;
+  static_assert(!VT || (DMA && (KPT == 2 || KPT == 4)), "transposed V needs 2 or 4 keys per thread");
+  u32x4 vst[KPT];
+  auto vt_load = [&](int t) {
+    const int kg = tid / CPR, cc = tid % CPR;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int gr = t * BC + kg * KPT + j;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (gr < N) z = *(const u32x4*)(V + (size_t)gr * D + cc * 8);
+      vst[j] = z;
+    }
+  };
+  auto vt_store = [&](int buf) {
+    char* sV = smem + (2 + buf) * TILEB;
+    const int kg = tid / CPR, cc = tid % CPR;
+    const int kbyte = kg * KPT * 2;  // byte offset of these keys in a V^T row
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * cc + i;
+      char* dst = sV + row * (BC * 2) + (((kbyte >> 4) ^ swz_vt<BC>(row)) << 4) + (kbyte & 15);
+      const int sh = 16 * (i & 1);
+      if constexpr (KPT == 4) {
+        u32x2 w2;
+        w2[0] = ((vst[0][i >> 1] >> sh) & 0xFFFFu) | (((vst[1][i >> 1] >> sh) & 0xFFFFu) << 16);
+        w2[1] = ((vst[2][i >> 1] >> sh) & 0xFFFFu) | (((vst[3][i >> 1] >> sh) & 0xFFFFu) << 16);
+        *(u32x2*)dst = w2;
+      } else {
+        *(unsigned*)dst = ((vst[0][i >> 1] >> sh) & 0xFFFFu) | (((vst[1][i >> 1] >> sh) & 0xFFFFu) << 16);
+      }
+    }
+  };
   auto gload = [&](int t) {
     const int k0 = t * BC;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < (DMA ? 0 : CPT); ++i) {
       const int ch = tid + NT * i;
       const int row = ch / CPR, cc = ch % CPR;
       const int gr = k0 + row;
@@ -204,7 +280,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     char* sK = smem + buf * TILEB;
     char* sV = smem + (2 + buf) * TILEB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < (DMA ? 0 : CPT); ++i) {
       const int ch = tid + NT * i;
       const int row = ch / CPR, cc = ch % CPR;
       *(u32x4*)(sK + row * ROWB + ((cc ^ swz_k16<D>(row)) << 4)) = stK[i];
@@ -213,8 +289,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   if (t_begin < t_end) {
-    gload(t_begin);
-    lstore(0);
+    if constexpr (DMA) {
+      dma(t_begin, 0);
+      if constexpr (VT) {
+        vt_load(t_begin);
+        vt_store(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS
+    } else {
+      gload(t_begin);
+      lstore(0);
+    }
   }
   __syncthreads();
 
@@ -229,12 +314,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int buf = (t - t_begin) & 1;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
-    if (t + 1 < t_end) gload(t + 1);
+    if (t + 1 < t_end) {
+      if constexpr (DMA) {
+        dma(t + 1, buf ^ 1);
+        if constexpr (VT) vt_load(t + 1);
+      } else {
+        gload(t + 1);
+      }
+    }
     const int k0 = t * BC;
 
     // Skip tiles that hold no allowed key for any row of this wave.
     if (wave_live && k0 < wk_hi && k0 + BC > wk_lo) {
-      // ---- S^T = K Q^T for BC keys x QW queries; each K read feeds QB MFMAs
+      // ---- S^T = K Q^T for BC keys x QW queries; each K read feeds QB MFMAs.
+      // K operands are double-buffered in registers one 16-wide chunk ahead,
+      // so each LDS read has KB*QB MFMAs of time to land.
       f32x16 sacc[QB][KB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -242,17 +336,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
+      bf16x8 kop[2][KB];
+      auto kread = [&](int kc, int slot) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int row = kb * 32 + l32;
-          const bf16x8 ka =
+          const int row = kb * 32 + (VT ? perm_rows(l32) : l32);
+          kop[slot][kb] =
               *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
+        }
+      };
+      kread(0, 0);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (kc + 1 < KC) kread(kc + 1, (kc + 1) & 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][kc], sacc[qb][kb], 0, 0, 0);
-        }
+            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc & 1][kb], qop[qb][kc], sacc[qb][kb], 0, 0, 0);
+        if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);  // next chunk's reads
+        __builtin_amdgcn_sched_group_barrier(0x008, KB * QB, 0);             // this chunk's MFMAs
+      }
+      __builtin_amdgcn_sched_barrier(0);
 
       // ---- mask, only where the tile is not fully visible to this wave
       if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + QW, k0, k0 + BC, a.window)) {
@@ -262,13 +367,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
           const int qi = qw0 + qb * 32 + l32;
           const int q_hi_key = MASK == MASK_CAUSAL ? min(qi, N - 1)
                                : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
-          const int hi_rel = q_hi_key - k0 - 4 * h;
-          const int lo_rel = (MASK == MASK_LOCAL ? qi - a.window : 0) - k0 - 4 * h;
+          const int hoff = VT ? 8 * h : 4 * h;
+          const int hi_rel = q_hi_key - k0 - hoff;
+          const int lo_rel = (MASK == MASK_LOCAL ? qi - a.window : 0) - k0 - hoff;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int kr = kb * 32 + acc_key(r);
+              const int kr = kb * 32 + (VT ? 16 * (r >> 3) + (r & 7) : acc_key(r));
               const bool ok =
                   (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
               sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
@@ -318,48 +424,71 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             for (int e = 0; e < 8; ++e) pop[qb][kb][u][e] = (bf16)sacc[qb][kb][8 * u + e];
         }
       };
-      // O^T += V^T P^T for one 32-key block; each V read feeds QB MFMAs
-      auto pv_block = [&](int kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
+      // O^T += V^T P^T for one 32-key block; each V read feeds QB MFMAs.
+      bf16x8 vop[2][DT];
+      auto vread = [&](int kb, int u) {
+        if constexpr (VT) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
-            const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
-            const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
-            const bf16x8 va = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][kb][u], oacc[qb][dt], 0, 0, 0);
+            const int row = dt * 32 + l32;
+            const int ch = (4 * kb + 2 * u + h) ^ swz_vt<BC>(row);
+            vop[u][dt] = *(const bf16x8*)(sV + row * (BC * 2) + ch * 16);
           }
+          return;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
+          vop[u][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       };
-      // Software pipeline over the key blocks: the PV MFMAs of block kb-1
-      // share a scheduling region with the exp / convert VALU work of block
-      // kb, interleaved a few VALU ops per MFMA, so the matrix core and the
-      // vector ALU of the wave run concurrently.
+      auto pv_mfma = [&](int kb, int u) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[qb][kb][u], oacc[qb][dt], 0, 0, 0);
+      };
+      // Software pipeline over the key blocks: block kb-1's V operands are
+      // read first, then its PV MFMAs share a scheduling region with the exp /
+      // convert VALU work of block kb (a few VALU ops per MFMA), so LDS
+      // latency, the matrix core and the vector ALU overlap.
       exp_block(0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 1; kb < KB; ++kb) {
-        pv_block(kb - 1);
-        exp_block(kb);
+      for (int kb = 1; kb <= KB; ++kb) {
+        vread(kb - 1, 0);
+        vread(kb - 1, 1);
+        if (kb < KB) exp_block(kb);
+        pv_mfma(kb - 1, 0);
+        pv_mfma(kb - 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, VT ? 2 * DT : 4 * DT, 0);  // all V reads of the block
+        if (kb < KB) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);     // VALU while they land
 #pragma unroll
-        for (int i = 0; i < 2 * DT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // 2 LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // QB MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x002, 28 * QB / DT, 0);  // VALU
+          for (int i = 0; i < 2 * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);      // QB MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 5 * QB, 0);  // VALU
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      pv_block(KB - 1);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb];
     }
 
-    if (t + 1 < t_end) lstore(buf ^ 1);
+    if constexpr (DMA) {
+      if constexpr (VT) {
+        if (t + 1 < t_end) vt_store(buf ^ 1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
+    } else {
+      if (t + 1 < t_end) lstore(buf ^ 1);
+    }
     __syncthreads();
   }
 
@@ -649,41 +778,42 @@ static hipError_t launch_fwd_bf16_pp(const FwdArgs& a0, int mask, hipStream_t st
   return hipGetLastError();
 }
 
-template <int D, int QB, int NW, int BC>
+template <int D, int QB, int NW, int BC, bool DMA = false, bool VT = false>
 static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t stream) {
   FwdArgs a = a0;
   constexpr int BR = NW * QB * 32;
   a.n_qtiles = (a.N + BR - 1) / BR;
   dim3 grid((unsigned)(a.n_qtiles * a.BH)), block(NW * 64);
   switch (mask) {
-    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
-    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_NONE>), grid, block, 0, stream, a); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_CAUSAL, DMA, VT>), grid, block, 0, stream, a); break;
+    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_LOCAL, DMA, VT>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_NONE, DMA, VT>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
-// Tile configurations (NW waves of QB x 32 query rows, BC keys per tile).
-// The default was picked by measurement on MI355X; the others stay
-// selectable for tuning sweeps.
+// Tile configurations (NW waves of QB x 32 query rows, BC keys per tile,
+// DMA = direct global->LDS staging, VT = transposed V tile). The default was
+// picked by interleaved timing on MI355X (causal 8192 x 128, 2048 x 64 and
+// the 16384 x 128 band); the others stay selectable for tuning sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
     switch (cfg) {
-      case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64>(a, mask, stream);
-      case 2: return launch_fwd_bf16_cfg<128, 2, 4, 64>(a, mask, stream);
-      case 3: return launch_fwd_bf16_cfg<128, 2, 4, 32>(a, mask, stream);
-      case 4: return launch_fwd_bf16_pp<128, 64>(a, mask, stream);
-      case 5: return launch_fwd_bf16_pp<128, 32>(a, mask, stream);
-      default: return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
+      case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64, true>(a, mask, stream);
+      case 2: return launch_fwd_bf16_cfg<128, 1, 8, 64, false>(a, mask, stream);
+      case 3: return launch_fwd_bf16_pp<128, 64>(a, mask, stream);
+      case 4: return launch_fwd_bf16_cfg<128, 1, 8, 64, true, true>(a, mask, stream);
+      case 5: return launch_fwd_bf16_cfg<128, 1, 4, 64, true>(a, mask, stream);
+      default: return launch_fwd_bf16_cfg<128, 1, 8, 128, true>(a, mask, stream);
     }
   }
   switch (cfg) {
-    case 1: return launch_fwd_bf16_cfg<64, 1, 8, 128>(a, mask, stream);
-    case 2: return launch_fwd_bf16_cfg<64, 2, 4, 64>(a, mask, stream);
-    case 3: return launch_fwd_bf16_cfg<64, 2, 4, 128>(a, mask, stream);
-    case 4: return launch_fwd_bf16_pp<64, 64>(a, mask, stream);
-    case 5: return launch_fwd_bf16_pp<64, 128>(a, mask, stream);
-    default: return launch_fwd_bf16_cfg<64, 1, 8, 64>(a, mask, stream);
+    case 1: return launch_fwd_bf16_cfg<64, 1, 8, 64, true>(a, mask, stream);
+    case 2: return launch_fwd_bf16_cfg<64, 1, 8, 64, false>(a, mask, stream);
+    case 3: return launch_fwd_bf16_pp<64, 64>(a, mask, stream);
+    case 4: return launch_fwd_bf16_cfg<64, 1, 8, 128, true, true>(a, mask, stream);
+    case 5: return launch_fwd_bf16_cfg<64, 1, 4, 64, true>(a, mask, stream);
+    default: return launch_fwd_bf16_cfg<64, 1, 8, 128, true>(a, mask, stream);
   }
 }
 
