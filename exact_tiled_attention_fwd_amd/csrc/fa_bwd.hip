@@ -22,6 +22,8 @@
 //     dS^T is the B operand of dQ^T += K^T dS^T (K read transposed).
 // Recomputing S and dP in step 3 costs two extra contractions (7 instead of
 // the 5 the gradient needs), the price of determinism without atomics.
+#include <stdlib.h>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -270,10 +272,249 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   }
 }
 
+// dK/dV, second form: eight waves (two per SIMD) of 32 keys each. To fit
+// two waves per SIMD next to the dK/dV accumulators, the V operand of
+// dP = dO V^T is read from an LDS copy of the workgroup's V rows (loaded
+// once) instead of registers; K stays in registers. Q/dO tiles arrive by
+// direct global->LDS loads, and every LDS operand is read one step ahead of
+// the MFMA that consumes it.
+template <int D>
+__device__ __forceinline__ int swz_rows(int row) {  // 16-byte chunk swizzle for row reads
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
+
+template <int D, int NW, int BRQ, int MASK>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
+  constexpr int BC = NW * 32;       // keys per workgroup (32 per wave)
+  constexpr int KC = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int QBN = BRQ / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int QTILEB = BRQ * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int NINS = BRQ * CPR / 64;  // 64-lane DMA instructions per query tile
+  static_assert((BRQ * CPR) % 64 == 0 && BRQ <= NW * 64, "tile must divide over the lanes");
+
+  __shared__ __attribute__((aligned(16))) char sVt[BC * ROWB];      // V rows of this workgroup
+  __shared__ __attribute__((aligned(16))) char sQO[4 * QTILEB];     // Q[2], dO[2]
+  __shared__ __attribute__((aligned(16))) float sL[2][BRQ];         // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][BRQ];         // D
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int n_kt = (N + BC - 1) / BC;
+  int w = blockIdx.x;
+  xcd_remap(w, a.BH * n_kt);
+  const int bh = w / n_kt;
+  const int kt = w - bh * n_kt;  // ascending: under a causal mask the first key tiles see most rows
+  const size_t base = (size_t)bh * N * D;
+  const bf16* __restrict__ Q = (const bf16*)a.q + base;
+  const bf16* __restrict__ K = (const bf16*)a.k + base;
+  const bf16* __restrict__ V = (const bf16*)a.v + base;
+  const bf16* __restrict__ dO = (const bf16*)a.dout + base;
+  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
+  const float* __restrict__ Dl = a.delta + (size_t)bh * N;
+  const int k0 = kt * BC;
+  const int kw0 = k0 + wv * 32;
+  const int key = kw0 + l32;
+
+  // this wave's 32 V rows -> LDS (rows past N clamped; their keys are never stored)
+#pragma unroll
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int p = j * 64 + lane;           // chunk index within the wave's rows
+    const int row = wv * 32 + p / CPR;     // row within the workgroup's V block
+    int gr = k0 + row;
+    gr = gr < N ? gr : N - 1;
+    const int cc = (p % CPR) ^ swz_rows<D>(row);
+    __builtin_amdgcn_global_load_lds(V + (size_t)gr * D + cc * 8,
+                                     (FA_LDS void*)(sVt + (wv * 32 * CPR + j * 64) * 16), 16, 0, 0);
+  }
+  bf16x8 kop[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < N) x = *(const u32x4*)(K + (size_t)key * D + kc * 16 + h * 8);
+    x = (x & a.q_and) ^ a.q_xor;  // sign / zero of the scale folded into K
+    kop[kc] = __builtin_bit_cast(bf16x8, x);
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+  const float c = a.scale_log2;
+  const float LOG2E = 1.4426950408889634f;
+
+  int q_lo = 0, q_hi = N;
+  if (MASK == MASK_CAUSAL) q_lo = k0;
+  if (MASK == MASK_LOCAL) {
+    q_lo = k0 - a.window > 0 ? k0 - a.window : 0;
+    const long long hh = (long long)k0 + BC + a.window;
+    q_hi = hh < N ? (int)hh : N;
+  }
+  const int t_begin = q_lo / BRQ, t_end = q_lo < q_hi ? (q_hi + BRQ - 1) / BRQ : t_begin;
+  // query rows that can see this wave's keys
+  int wq_lo = 0, wq_hi = N;
+  if (MASK == MASK_CAUSAL) wq_lo = kw0;
+  if (MASK == MASK_LOCAL) {
+    wq_lo = kw0 - a.window;
+    wq_hi = kw0 + 32 + a.window;
+  }
+  const bool wave_live = kw0 < N;
+
+  auto dma = [&](int t, int buf) {
+    char* sQ = sQO + buf * QTILEB;
+    char* sO = sQO + (2 + buf) * QTILEB;
+    for (int ins = wv; ins < NINS; ins += NW) {
+      const int slot = ins * 64;
+      const int p = slot + lane;
+      const int row = p / CPR;
+      int gr = t * BRQ + row;
+      gr = gr < N ? gr : N - 1;
+      const int cc = (p % CPR) ^ swz_dual<D>(row);
+      __builtin_amdgcn_global_load_lds(Q + (size_t)gr * D + cc * 8, (FA_LDS void*)(sQ + slot * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dO + (size_t)gr * D + cc * 8, (FA_LDS void*)(sO + slot * 16), 16, 0, 0);
+    }
+  };
+  float stL = 0.f, stD = 0.f;
+  auto ld_stats = [&](int t) {
+    if (tid < BRQ) {
+      const int gr = t * BRQ + tid;
+      stL = gr < N ? LSE[gr] * LOG2E : INFINITY;  // padded rows get P = 0
+      stD = gr < N ? Dl[gr] : 0.f;
+    }
+  };
+  auto st_stats = [&](int buf) {
+    if (tid < BRQ) {
+      sL[buf][tid] = stL;
+      sD[buf][tid] = stD;
+    }
+  };
+
+  if (t_begin < t_end) {
+    dma(t_begin, 0);
+    ld_stats(t_begin);
+    st_stats(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V rows and the first tile are in LDS
+  __syncthreads();
+
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+  const int vrow = wv * 32 + l32;  // this lane's V row in sVt
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const char* sQ = sQO + buf * QTILEB;
+    const char* sO = sQO + (2 + buf) * QTILEB;
+    if (t + 1 < t_end) {
+      dma(t + 1, buf ^ 1);
+      ld_stats(t + 1);
+    }
+    const int q0 = t * BRQ;
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+      const int qr0 = q0 + qb * 32;
+      if (!(wave_live && qr0 < wq_hi && qr0 + 32 > wq_lo)) continue;  // no allowed pair
+      // S = Q K^T and dP = dO V^T (lane <-> key, 16 query rows); operands
+      // read one 16-wide chunk ahead
+      f32x16 sa, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sa[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const int arow = qb * 32 + l32;
+      bf16x8 qa[2], oa[2], va[2];
+      auto rd = [&](int kc, int sl) {
+        const int off = arow * ROWB + (((2 * kc + h) ^ swz_dual<D>(arow)) << 4);
+        qa[sl] = *(const bf16x8*)(sQ + off);
+        oa[sl] = *(const bf16x8*)(sO + off);
+        va[sl] = *(const bf16x8*)(sVt + vrow * ROWB + (((2 * kc + h) ^ swz_rows<D>(vrow)) << 4));
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (kc + 1 < KC) rd(kc + 1, (kc + 1) & 1);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kc & 1], kop[kc], sa, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kc & 1], va[kc & 1], dp, 0, 0, 0);
+        if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const bool need_mask = !tile_full<MASK>(qr0, qr0 + 32, kw0, kw0 + 32, a.window);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 L4 = *(const f32x4*)&sL[buf][qb * 32 + 8 * rr + 4 * h];
+        const f32x4 D4 = *(const f32x4*)&sD[buf][qb * 32 + 8 * rr + 4 * h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float sv = sa[r];
+          if (need_mask && !allowed<MASK>(qr0 + 8 * rr + 4 * h + e, key, a.window)) sv = -INFINITY;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -L4[e]));
+          sa[r] = pv;
+          dp[r] = pv * (dp[r] - D4[e]);
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q; B operands by transposed reads
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pa, da;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pa[e] = (bf16)sa[8 * u + e];
+          da[e] = (bf16)dp[8 * u + e];
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = qb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rhi) << 1)) * 8;
+          const i16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sO + rlo * ROWB + clo));
+          const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sO + rhi * ROWB + chi));
+          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sQ + rlo * ROWB + clo));
+          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sQ + rhi * ROWB + chi));
+          const bf16x8 ob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 qbv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ob, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qbv, dk[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < t_end) st_stats(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed in LDS
+    __syncthreads();
+  }
+
+  bf16* __restrict__ dK = (bf16*)a.dk + base;
+  bf16* __restrict__ dV = (bf16*)a.dv + base;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kr = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (kr < N) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dK[(size_t)kr * D + dt * 32 + l32] = (bf16)(dk[dt][r] * a.scale);
+        dV[(size_t)kr * D + dt * 32 + l32] = (bf16)dv[dt][r];
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------- dQ
+// Query-major, laid out like the forward: S^T = K Q^T and dP^T = V dO^T put
+// the query on the lane, so LSE_i and D_i are per-lane scalars, and dS^T is
+// the B operand of dQ^T += K^T dS^T (K read transposed). K/V tiles arrive
+// by direct global->LDS loads; operands are read one step ahead.
 template <int D, int NW, int BC, int MASK>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
-  constexpr int NT = NW * 64;
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BR = NW * 32;
   constexpr int KC = D / 16;
   constexpr int DT = D / 32;
@@ -281,8 +522,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
   constexpr int CPR = D / 8;
-  constexpr int CPT = BC * CPR / NT;
-  static_assert((BC * CPR) % NT == 0, "tile chunks must divide evenly");
+  constexpr int NINS = BC * CPR / 64;  // 64-lane DMA instructions per tile
+  static_assert((BC * CPR) % 64 == 0, "tile chunks must divide evenly");
 
   __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2] (dual), V[2]
 
@@ -329,40 +570,26 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   int k_lo, k_hi;
   key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
   const int t_begin = k_lo / BC, t_end = (k_hi + BC - 1) / BC;
+  int wk_lo, wk_hi;
+  key_range<MASK>(qw0, qw0 + 32, N, a.window, wk_lo, wk_hi);
+  const bool wave_live = qw0 < N;
 
-  u32x4 stK[CPT], stV[CPT];
-  auto gload = [&](int t) {
-    const int r0 = t * BC;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int gr = r0 + row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (gr < N) {
-        zk = *(const u32x4*)(K + (size_t)gr * D + cc * 8);
-        zv = *(const u32x4*)(V + (size_t)gr * D + cc * 8);
-      }
-      stK[i] = zk;
-      stV[i] = zv;
-    }
-  };
-  auto lstore = [&](int buf) {
+  auto dma = [&](int t, int buf) {
     char* sK = smem + buf * TILEB;
     char* sV = smem + (2 + buf) * TILEB;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int off = row * ROWB + ((cc ^ swz_dual<D>(row)) << 4);
-      *(u32x4*)(sK + off) = stK[i];
-      *(u32x4*)(sV + off) = stV[i];
+    for (int ins = wv; ins < NINS; ins += NW) {
+      const int slot = ins * 64;
+      const int p = slot + lane;
+      const int row = p / CPR;
+      int gr = t * BC + row;
+      gr = gr < N ? gr : N - 1;  // keys past N are masked
+      const int cc = (p % CPR) ^ swz_dual<D>(row);
+      __builtin_amdgcn_global_load_lds(K + (size_t)gr * D + cc * 8, (FA_LDS void*)(sK + slot * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(V + (size_t)gr * D + cc * 8, (FA_LDS void*)(sV + slot * 16), 16, 0, 0);
     }
   };
-  if (t_begin < t_end) {
-    gload(t_begin);
-    lstore(0);
-  }
+  if (t_begin < t_end) dma(t_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   const int g16 = lane >> 4, s16 = lane & 15;
@@ -373,60 +600,70 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
     const int buf = (t - t_begin) & 1;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
-    if (t + 1 < t_end) gload(t + 1);
+    if (t + 1 < t_end) dma(t + 1, buf ^ 1);
     const int k0 = t * BC;
-    bf16x8 dsb[KB][2];
+    if (wave_live && k0 < wk_hi && k0 + BC > wk_lo) {
+      bf16x8 dsb[KB][2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      f32x16 s, dp;
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x16 sa, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const int arow = kb * 32 + l32;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int off = arow * ROWB + (((2 * kc + h) ^ swz_dual<D>(arow)) << 4);
-        const bf16x8 ka = *(const bf16x8*)(sK + off);
-        const bf16x8 va = *(const bf16x8*)(sV + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[kc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, oop[kc], dp, 0, 0, 0);
-      }
-      const int kb0 = k0 + kb * 32;
-      const bool need_mask =
-          (kb0 + 32 > N) || !tile_full<MASK>(qw0, qw0 + 32, kb0, kb0 + 32, a.window);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = s[r];
-        if (need_mask) {
-          const int kk = kb0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (!(kk < N && allowed<MASK>(qi, kk, a.window))) sv = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          sa[r] = 0.f;
+          dp[r] = 0.f;
         }
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -Lq));
-        s[r] = p * (dp[r] - Dq);
+        const int arow = kb * 32 + l32;
+        bf16x8 ka[2], va[2];
+        auto rd = [&](int kc, int sl) {
+          const int off = arow * ROWB + (((2 * kc + h) ^ swz_dual<D>(arow)) << 4);
+          ka[sl] = *(const bf16x8*)(sK + off);
+          va[sl] = *(const bf16x8*)(sV + off);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          if (kc + 1 < KC) rd(kc + 1, (kc + 1) & 1);
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kc & 1], qop[kc], sa, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kc & 1], oop[kc], dp, 0, 0, 0);
+          if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb0 = k0 + kb * 32;
+        const bool need_mask =
+            (kb0 + 32 > N) || !tile_full<MASK>(qw0, qw0 + 32, kb0, kb0 + 32, a.window);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float sv = sa[r];
+          if (need_mask) {
+            const int kk = kb0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (!(kk < N && allowed<MASK>(qi, kk, a.window))) sv = -INFINITY;
+          }
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -Lq));
+          sa[r] = pv * (dp[r] - Dq);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dsb[kb][u][e] = (bf16)sa[8 * u + e];
       }
+      // dQ^T += K^T dS^T (K read transposed)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsb[kb][u][e] = (bf16)s[8 * u + e];
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+            const int clo = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rlo) << 1)) * 8;
+            const int chi = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rhi) << 1)) * 8;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sK + rlo * ROWB + clo));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sK + rhi * ROWB + chi));
+            const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb[kb][u], dq[dt], 0, 0, 0);
+          }
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
-          const int clo = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rlo) << 1)) * 8;
-          const int chi = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rhi) << 1)) * 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sK + rlo * ROWB + clo));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sK + rhi * ROWB + chi));
-          const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsb[kb][u], dq[dt], 0, 0, 0);
-        }
-    if (t + 1 < t_end) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed in LDS
     __syncthreads();
   }
 
@@ -584,8 +821,9 @@ __global__ __launch_bounds__(F32B_T) void bwd_dq_f32_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ launch
 template <int D, int MASK>
-static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, hipStream_t stream) {
-  constexpr int KV_NW = 4, KV_BRQ = 64;   // 128 keys per dK/dV workgroup
+static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, int cfg, hipStream_t stream) {
+  constexpr int KV_NW = 4, KV_BRQ = 64;   // first form: 128 keys per dK/dV workgroup
+  constexpr int KV2_NW = 8, KV2_BRQ = 32; // second form: 256 keys per dK/dV workgroup
   constexpr int Q_NW = 8, Q_BC = 64;      // 256 query rows per dQ workgroup
   const long rows = (long)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
@@ -593,9 +831,15 @@ static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, hipStream_t stream) {
                      0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_kt = (a.N + KV_NW * 32 - 1) / (KV_NW * 32);
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, KV_NW, KV_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
-                     dim3(KV_NW * 64), 0, stream, a);
+  if (cfg == 1) {
+    const int n_kt = (a.N + KV_NW * 32 - 1) / (KV_NW * 32);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, KV_NW, KV_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
+                       dim3(KV_NW * 64), 0, stream, a);
+  } else {
+    const int n_kt = (a.N + KV2_NW * 32 - 1) / (KV2_NW * 32);
+    hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<D, KV2_NW, KV2_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
+                       dim3(KV2_NW * 64), 0, stream, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.N + Q_NW * 32 - 1) / (Q_NW * 32);
@@ -624,8 +868,10 @@ static hipError_t launch_bwd_f32_mask(const BwdArgs& a, hipStream_t stream) {
 template <int MASK>
 static hipError_t launch_bwd_mask(const BwdArgs& a, int bf16_path, hipStream_t stream) {
   if (bf16_path) {
-    if (a.d == 128) return launch_bwd_bf16_mask<128, MASK>(a, stream);
-    return launch_bwd_bf16_mask<64, MASK>(a, stream);
+    const char* env = getenv("FA_BWD_CFG");  // tuning only: 1 selects the first dK/dV form
+    const int cfg = env ? atoi(env) : 0;
+    if (a.d == 128) return launch_bwd_bf16_mask<128, MASK>(a, cfg, stream);
+    return launch_bwd_bf16_mask<64, MASK>(a, cfg, stream);
   }
   if (a.d <= 8) return launch_bwd_f32_mask<8, MASK>(a, stream);
   if (a.d <= 32) return launch_bwd_f32_mask<32, MASK>(a, stream);
