@@ -328,8 +328,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
     int gr = k0 + row;
     gr = gr < N ? gr : N - 1;
     const int cc = (p % CPR) ^ swz_rows<D>(row);
-    __builtin_amdgcn_global_load_lds(V + (size_t)gr * D + cc * 8,
-                                     (FA_LDS void*)(sVt + (wv * 32 * CPR + j * 64) * 16), 16, 0, 0);
+    lds_dma16(V + (size_t)gr * D + cc * 8, lds_addr(sVt + (wv * 32 * CPR + j * 64) * 16));
   }
   bf16x8 kop[KC];
 #pragma unroll
@@ -377,8 +376,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
       int gr = t * BRQ + row;
       gr = gr < N ? gr : N - 1;
       const int cc = (p % CPR) ^ swz_dual<D>(row);
-      __builtin_amdgcn_global_load_lds(Q + (size_t)gr * D + cc * 8, (FA_LDS void*)(sQ + slot * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dO + (size_t)gr * D + cc * 8, (FA_LDS void*)(sO + slot * 16), 16, 0, 0);
+      lds_dma16(Q + (size_t)gr * D + cc * 8, lds_addr(sQ + slot * 16));
+      lds_dma16(dO + (size_t)gr * D + cc * 8, lds_addr(sO + slot * 16));
     }
   };
   float stL = 0.f, stD = 0.f;
@@ -584,8 +583,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
       int gr = t * BC + row;
       gr = gr < N ? gr : N - 1;  // keys past N are masked
       const int cc = (p % CPR) ^ swz_dual<D>(row);
-      __builtin_amdgcn_global_load_lds(K + (size_t)gr * D + cc * 8, (FA_LDS void*)(sK + slot * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(V + (size_t)gr * D + cc * 8, (FA_LDS void*)(sV + slot * 16), 16, 0, 0);
+      lds_dma16(K + (size_t)gr * D + cc * 8, lds_addr(sK + slot * 16));
+      lds_dma16(V + (size_t)gr * D + cc * 8, lds_addr(sV + slot * 16));
     }
   };
   if (t_begin < t_end) dma(t_begin, 0);

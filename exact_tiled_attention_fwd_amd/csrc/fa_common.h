@@ -16,6 +16,23 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 namespace fa {
 
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(FA_LDS const char*)p;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's chunk lands at lds_base + 16 i, lds_base wave-uniform (M0).
+// Issued as inline assembly so that the compiler does not make later LDS
+// reads of other buffers wait for it; callers wait with vmcnt(0) themselves
+// before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr)
+               : "memory", "m0");
+}
+
 // Mask modes, mirroring fa_mask.
 enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_LOCAL = 2 };
 

@@ -218,10 +218,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       int gr = k0 + row;
       gr = gr < N ? gr : N - 1;
       const int ck = (p % CPR) ^ swz_k16<D>(row);
-      __builtin_amdgcn_global_load_lds(K + (size_t)gr * D + ck * 8, (FA_LDS void*)(sK + slot * 16), 16, 0, 0);
+      lds_dma16(K + (size_t)gr * D + ck * 8, lds_addr(sK + slot * 16));
       if constexpr (!VT) {
         const int cv = (p % CPR) ^ swz_v16<D>(row);
-        __builtin_amdgcn_global_load_lds(V + (size_t)gr * D + cv * 8, (FA_LDS void*)(sV + slot * 16), 16, 0, 0);
+        lds_dma16(V + (size_t)gr * D + cv * 8, lds_addr(sV + slot * 16));
       }
     }
   };
@@ -537,8 +537,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
   constexpr int CPR = D / 8;
-  constexpr int CPT = BC * CPR / NT;
-  static_assert((BC * CPR) % NT == 0, "tile chunks must divide evenly");
+  constexpr int CPW = BC * CPR / NT;  // DMA chunks per lane per tile
+  static_assert((BC * CPR) % NT == 0 && CPW >= 1, "tile chunks must divide evenly");
 
   __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2], V[2]
 
@@ -593,44 +593,17 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
                        : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
   const int q_lo_key = MASK == MASK_LOCAL ? qi - a.window : 0;
 
-  // staging of K_{i+1} and V_i (global -> registers -> LDS)
-  u32x4 stK[CPT], stV[CPT];
-  auto gload_k = [&](int j) {
+  // direct global->LDS staging of K_j (buffer j&1) or V_j (buffer 2 + (j&1))
+  auto dma = [&](const bf16* __restrict__ src, int j, char* dst_tile, bool vrow) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int gr = (tb + j) * BC + ch / CPR;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (j < T && gr < N) z = *(const u32x4*)(K + (size_t)gr * D + (ch % CPR) * 8);
-      stK[i] = z;
-    }
-  };
-  auto gload_v = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int gr = (tb + j) * BC + ch / CPR;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (j < T && gr < N) z = *(const u32x4*)(V + (size_t)gr * D + (ch % CPR) * 8);
-      stV[i] = z;
-    }
-  };
-  auto lstore_k = [&](int j) {
-    char* sK = smem + (j & 1) * TILEB;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      *(u32x4*)(sK + row * ROWB + ((cc ^ swz_k16<D>(row)) << 4)) = stK[i];
-    }
-  };
-  auto lstore_v = [&](int j) {
-    char* sV = smem + (2 + (j & 1)) * TILEB;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      *(u32x4*)(sV + row * ROWB + ((cc ^ swz_v16<D>(row)) << 4)) = stV[i];
+    for (int i = 0; i < CPW; ++i) {
+      const int slot = (wv * CPW + i) * 64;
+      const int p = slot + lane;
+      const int row = p / CPR;
+      int gr = (tb + j) * BC + row;
+      gr = gr < N ? gr : N - 1;  // keys past N are masked
+      const int cc = (p % CPR) ^ (vrow ? swz_v16<D>(row) : swz_k16<D>(row));
+      lds_dma16(src + (size_t)gr * D + cc * 8, lds_addr(dst_tile + slot * 16));
     }
   };
 
@@ -641,39 +614,65 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
   f32x16 sacc[KB];
   bf16x8 pop[KB][2];
 
-  auto qk = [&](int j) {
+  // MFMA phase j: scores of tile j and P V of tile j-1, operands prefetched
+  auto mfma_phase = [&](int j) {
+    const bool doqk = active(j), dopv = active(j - 1);
     const char* sK = smem + (j & 1) * TILEB;
+    const char* sV = smem + (2 + ((j - 1) & 1)) * TILEB;
+    bf16x8 vop[2][DT];
+    auto vread = [&](int kb, int u) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int dt = 0; dt < DT; ++dt) {
+        const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+        const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+        const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
+        vop[u][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    if (doqk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      bf16x8 kop[2][KB];
+      auto kread = [&](int kc, int slot) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int row = kb * 32 + l32;
+          kop[slot][kb] = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
+        }
+      };
+      kread(0, 0);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (kc + 1 < KC) kread(kc + 1, (kc + 1) & 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc & 1][kb], qop[kc], sacc[kb], 0, 0, 0);
+        if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (dopv) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int row = kb * 32 + l32;
-        const bf16x8 ka =
-            *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[kc], sacc[kb], 0, 0, 0);
+        vread(kb, 0);
+        vread(kb, 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[kb][u], oacc[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * DT, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
   };
-  auto pv = [&](int j) {
-    const char* sV = smem + (2 + (j & 1)) * TILEB;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
-          const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
-          const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[kb][u], oacc[dt], 0, 0, 0);
-        }
-  };
+  // VALU phase: online softmax of tile j (its scores are in sacc)
   auto softmax = [&](int j) {
     const int k0 = (tb + j) * BC;
     if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + 32, k0, k0 + BC, a.window)) {
@@ -718,33 +717,29 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
     l_run += ls;
   };
 
-  // prologue: K_0 resident; K_1, V_0 in flight
-  gload_k(0);
-  lstore_k(0);
-  gload_k(1);
-  gload_v(0);
+  // prologue: K_0 resident
+  dma(K, 0, smem, false);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
+  // Global phase f: group 0 runs MFMA phase f/2 on even f, group 1 MFMA
+  // phase (f-1)/2 on odd f; each group's VALU phase follows its MFMA phase.
+  // K_j is read in phases 2j, 2j+1 and V_j in 2j+2, 2j+3; even phase 2i
+  // starts the loads of K_{i+1} and V_i (their buffers were last read in
+  // phase 2i-1) and odd phase 2i+1 waits for them before its barrier.
   for (int f = 0; f < 2 * T + 2; ++f) {
-    const bool mfma_phase = ((f & 1) == grp);
-    const int j = (f - grp) >> 1;  // this wave's step (MFMA phase j, or VALU phase j-?)
-    if (mfma_phase) {
-      // MFMA phase j: scores of tile j, P V of tile j-1
-      if (active(j)) qk(j);
-      if (active(j - 1)) pv(j - 1);
+    if ((f & 1) == 0) {
+      const int i = f >> 1;
+      if (i + 1 < T) dma(K, i + 1, smem + ((i + 1) & 1) * TILEB, false);
+      if (i < T) dma(V, i, smem + (2 + (i & 1)) * TILEB, true);
+    }
+    if ((f & 1) == grp) {
+      mfma_phase((f - grp) >> 1);
     } else {
-      // VALU phase: softmax of the tile whose scores the last MFMA phase made
       const int js = grp == 0 ? (f - 1) >> 1 : (f >> 1) - 1;
       if (active(js)) softmax(js);
     }
-    if (f & 1) {
-      // odd phase 2i+1: store K_{i+1} and V_i, start loading K_{i+2}, V_{i+1}
-      const int i = f >> 1;
-      lstore_k(i + 1);
-      lstore_v(i);
-      gload_k(i + 2);
-      gload_v(i + 1);
-    }
+    if (f & 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K_{i+1}, V_i landed
     __syncthreads();
   }
 
@@ -802,6 +797,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
       case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64, true>(a, mask, stream);
       case 2: return launch_fwd_bf16_cfg<128, 1, 8, 64, false>(a, mask, stream);
       case 3: return launch_fwd_bf16_pp<128, 64>(a, mask, stream);
+      case 6: return launch_fwd_bf16_pp<128, 128>(a, mask, stream);
       case 4: return launch_fwd_bf16_cfg<128, 1, 8, 64, true, true>(a, mask, stream);
       case 5: return launch_fwd_bf16_cfg<128, 1, 4, 64, true>(a, mask, stream);
       default: return launch_fwd_bf16_cfg<128, 1, 8, 128, true>(a, mask, stream);
@@ -811,6 +807,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
     case 1: return launch_fwd_bf16_cfg<64, 1, 8, 64, true>(a, mask, stream);
     case 2: return launch_fwd_bf16_cfg<64, 1, 8, 64, false>(a, mask, stream);
     case 3: return launch_fwd_bf16_pp<64, 64>(a, mask, stream);
+    case 6: return launch_fwd_bf16_pp<64, 128>(a, mask, stream);
     case 4: return launch_fwd_bf16_cfg<64, 1, 8, 128, true, true>(a, mask, stream);
     case 5: return launch_fwd_bf16_cfg<64, 1, 4, 64, true>(a, mask, stream);
     default: return launch_fwd_bf16_cfg<64, 1, 8, 128, true>(a, mask, stream);
