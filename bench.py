@@ -8,11 +8,16 @@ forward-only figure of the causal [2, 16, 8192, 128] workload, the roofline
 of the dominant kernel, and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --summarize-pmc DIR --copy-mib M   (HBM traffic summary, no GPU)
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -64,6 +69,98 @@ def bwd_bytes(w):
     return 8 * B * H * N * d * es + B * H * N * 4
 
 
+def kernel_source_sha():
+    """Hash of the HIP sources: HBM traffic counters taken on other sources
+    are not reported."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc", "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# Entry point each kernel belongs to (one fa_bwd call = three launches).
+UNIT_OF_KERNEL = (("fwd_bf16", "fa_fwd"), ("fwd_f32", "fa_fwd"), ("bwd_pre", "fa_bwd"),
+                  ("bwd_dkdv", "fa_bwd"), ("bwd_dq", "fa_bwd"))
+TRAFFIC_TAG = "traffic-json:"
+
+
+def _pmc_per_dispatch(path, counter):
+    """Mean over dispatches of one counter, per kernel name (KiB)."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {n: sum(v) / len(v) for n, v in out.items()}
+
+
+def summarize_pmc(d, copy_mib):
+    """Markdown summary of the FETCH_SIZE / WRITE_SIZE passes in directory d:
+    bench run (fetch_*, write_*) and the copy calibration (copy_fetch_*,
+    copy_write_*). Counter readings are scaled so that the plain copy of
+    copy_mib MiB reads and writes exactly that many bytes."""
+    one = lambda pat: sorted(glob.glob(os.path.join(d, pat)))[0]
+    cf = _pmc_per_dispatch(one("copy_fetch*_counter_collection.csv"), "FETCH_SIZE")
+    cw = _pmc_per_dispatch(one("copy_write*_counter_collection.csv"), "WRITE_SIZE")
+    ck = [n for n in cf if "copyBuffer" in n or "copy" in n.lower()][0]
+    nbytes = copy_mib * (1 << 20)
+    f_fetch = nbytes / (cf[ck] * 1024.0)
+    f_write = nbytes / (cw[ck] * 1024.0)
+    fe = _pmc_per_dispatch(one("fetch*_counter_collection.csv"), "FETCH_SIZE")
+    wr = _pmc_per_dispatch(one("write*_counter_collection.csv"), "WRITE_SIZE")
+    units, rows = {}, []
+    for name in sorted(fe):
+        unit = next((u for key, u in UNIT_OF_KERNEL if key in name), None)
+        if unit is None:
+            continue
+        rb = fe[name] * 1024.0 * f_fetch
+        wb = wr.get(name, 0.0) * 1024.0 * f_write
+        rows.append((name, fe[name], wr.get(name, 0.0), rb, wb))
+        u = units.setdefault(unit, {"read_bytes": 0.0, "write_bytes": 0.0})
+        u["read_bytes"] += rb
+        u["write_bytes"] += wb
+    lines = ["| Kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | read bytes | written bytes |",
+             "|---|---|---|---|---|"]
+    for name, f_, w_, rb, wb in rows:
+        short = re.sub(r"\(.*", "", name)
+        lines.append(f"| `{short}` | {f_:.0f} | {w_:.0f} | {rb / 1e6:.1f} MB | {wb / 1e6:.1f} MB |")
+    meta = {"source_sha": kernel_source_sha(), "fetch_factor": round(f_fetch, 4),
+            "write_factor": round(f_write, 4),
+            "units": {u: {k: round(v) for k, v in x.items()} for u, x in units.items()}}
+    lines += ["", f"Calibration: the {copy_mib} MiB copy (`{ck}`) reads {cf[ck]:.0f} KiB and writes "
+              f"{cw[ck]:.0f} KiB by the counters, so FETCH_SIZE is scaled by {f_fetch:.3f} and "
+              f"WRITE_SIZE by {f_write:.3f}.", ""]
+    for u, x in units.items():
+        lines.append(f"- `{u}` per call: {x['read_bytes'] / 1e6:.1f} MB read + "
+                     f"{x['write_bytes'] / 1e6:.1f} MB written from/to HBM")
+    lines += ["", f"<!-- {TRAFFIC_TAG} {json.dumps(meta)} -->"]
+    return "\n".join(lines)
+
+
+def load_traffic(unit):
+    """HBM bytes per call of `unit` from the committed counter summary, or
+    None when the summary was taken on different kernel sources."""
+    sha = kernel_source_sha()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            text = f.read()
+        m = re.search(re.escape(TRAFFIC_TAG) + r"\s*(\{.*\})\s*-->", text)
+        if not m:
+            continue
+        meta = json.loads(m.group(1))
+        if meta.get("source_sha") == sha and unit in meta.get("units", {}):
+            x = meta["units"][unit]
+            return int(x["read_bytes"] + x["write_bytes"]), os.path.relpath(path, ROOT)
+    return None, None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,7 +174,14 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(calibrates the HBM byte counters)")
+    ap.add_argument("--summarize-pmc", default=None,
+                    help="print the HBM traffic summary of the rocprofv3 counter CSVs in DIR")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of the calibration copy used with --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc, args.copy_mib))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
               "communication, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
@@ -149,9 +253,11 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n][0])
     ms_dom, fl_dom, by_dom = kernels[dom]
     achieved = fl_dom / (ms_dom * 1e-3) / 1e12
+    traffic, traffic_src = load_traffic(dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": dom,
+                "traffic": traffic, "traffic_unit": "bytes per call", "traffic_source": traffic_src,
+                "algorithmic_bytes_per_launch": by_dom, "kernel": dom,
                 "algorithmic_flop_per_launch": fl_dom,
                 "avg_launch_us": round(ms_dom * 1e3, 2)}
 
@@ -231,21 +337,26 @@ def cpu_baseline(w, inp, have_bwd):
     """The CPU oracle (plain double C, OpenMP) on one (batch, head) slice of
     the same workload: dense forward over all rows plus, when the step has a
     backward, the dense backward of that slice."""
-    import numpy as np
     import oracle
     B, H, N, d = w.shape
-    sl = {n: inp[n].reshape(B * H, N, d)[:1] for n in ("q", "k", "v", "dout")}
-    t0 = time.perf_counter()
-    oracle.fwd_dense(sl["q"], sl["k"], sl["v"], w.scale, w.mask, w.window)
-    if have_bwd:
-        oracle.bwd_dense(sl["q"], sl["k"], sl["v"], sl["dout"], w.scale, w.mask, w.window)
-    sec = time.perf_counter() - t0
+    flat = {n: inp[n].reshape(B * H, N, d) for n in ("q", "k", "v", "dout")}
     one = type(w)(**{**w.__dict__, "B": 1, "H": 1})
-    flops = fwd_flops(one) + (bwd_flops(one) if have_bwd else 0.0)
+    flops_slice = fwd_flops(one) + (bwd_flops(one) if have_bwd else 0.0)
+    # slices one after another until about TARGET_S seconds of CPU work
+    TARGET_S = 12.0
+    t0 = time.perf_counter()
+    n = 0
+    while n < B * H and (time.perf_counter() - t0) < TARGET_S:
+        sl = {k_: t[n:n + 1] for k_, t in flat.items()}
+        oracle.fwd_dense(sl["q"], sl["k"], sl["v"], w.scale, w.mask, w.window)
+        if have_bwd:
+            oracle.bwd_dense(sl["q"], sl["k"], sl["v"], sl["dout"], w.scale, w.mask, w.window)
+        n += 1
+    sec = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+    return {"value": round(n * flops_slice / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"one (b,h) slice [1,1,{N},{d}] of {w.name}: dense forward"
+            "sample": f"{n} of {B * H} (b,h) slices [1,1,{N},{d}] of {w.name}: dense forward"
                       + (" + dense backward" if have_bwd else "") + ", float64"}
 
 

@@ -417,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
       ld_stats(t + 1);
     }
     const int q0 = t * BRQ;
-#pragma unroll
+#pragma unroll 1
     for (int qb = 0; qb < QBN; ++qb) {
       const int qr0 = q0 + qb * 32;
       if (!(wave_live && qr0 < wq_hi && qr0 + 32 > wq_lo)) continue;  // no allowed pair
@@ -645,10 +645,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 8; ++e) dsb[kb][u][e] = (bf16)sa[8 * u + e];
-      }
-      // dQ^T += K^T dS^T (K read transposed)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        // dQ^T += K^T dS^T for this key block (K read transposed)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -661,6 +658,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
             const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb[kb][u], dq[dt], 0, 0, 0);
           }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed in LDS
     __syncthreads();
