@@ -41,9 +41,6 @@ __device__ __forceinline__ int swz_dual(int row) {
   }
 }
 
-__device__ __forceinline__ void xcd_remap(int& w, int total) {
-  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
-}
 
 // ---------------------------------------------------------------- preprocess
 // D_i = <dO_i, O_i> in float32; d/8 threads per row, 16 bytes each.
@@ -88,10 +85,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int l32 = lane & 31, h = lane >> 5;
   const int N = a.N;
   const int n_kt = (N + BC - 1) / BC;
-  int w = blockIdx.x;
-  xcd_remap(w, a.BH * n_kt);
-  const int bh = w / n_kt;
-  const int kt = w - bh * n_kt;  // ascending: under a causal mask the first key tiles see most rows
+  int bh, kt;  // ascending: under a causal mask the first key tiles see most rows
+  wg_tile(blockIdx.x, a.BH, n_kt, bh, kt);
   const size_t base = (size_t)bh * N * D;
   const bf16* __restrict__ Q = (const bf16*)a.q + base;
   const bf16* __restrict__ K = (const bf16*)a.k + base;
@@ -305,10 +300,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
   const int l32 = lane & 31, h = lane >> 5;
   const int N = a.N;
   const int n_kt = (N + BC - 1) / BC;
-  int w = blockIdx.x;
-  xcd_remap(w, a.BH * n_kt);
-  const int bh = w / n_kt;
-  const int kt = w - bh * n_kt;  // ascending: under a causal mask the first key tiles see most rows
+  int bh, kt;  // ascending: under a causal mask the first key tiles see most rows
+  wg_tile(blockIdx.x, a.BH, n_kt, bh, kt);
   const size_t base = (size_t)bh * N * D;
   const bf16* __restrict__ Q = (const bf16*)a.q + base;
   const bf16* __restrict__ K = (const bf16*)a.k + base;
@@ -530,10 +523,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int l32 = lane & 31, h = lane >> 5;
   const int N = a.N;
   const int n_qt = (N + BR - 1) / BR;
-  int w = blockIdx.x;
-  xcd_remap(w, a.BH * n_qt);
-  const int bh = w / n_qt;
-  int qt = w - bh * n_qt;
+  int bh, qt;
+  wg_tile(blockIdx.x, a.BH, n_qt, bh, qt);
   if (MASK == MASK_CAUSAL) qt = n_qt - 1 - qt;
   const size_t base = (size_t)bh * N * D;
   const bf16* __restrict__ Q = (const bf16*)a.q + base;

@@ -33,6 +33,28 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_base) {
                : "memory", "m0");
 }
 
+// Workgroup id -> (head, tile rank); rank 0 is launched first.
+// Workgroup ids are handed to the eight XCDs round-robin, so id w is the
+// (w / 8)-th workgroup that XCD x = w % 8 runs. When the heads split evenly
+// over the XCDs, every XCD gets a contiguous run of heads (their K/V stay in
+// that XCD's L2) and walks them rank-major: rank 0 of each of its heads,
+// then rank 1, ... so that the longest tiles of all its heads start first
+// and the short ones fill in at the end. Otherwise the ids map head-major,
+// which spreads each head's ranks over all XCDs.
+__device__ __forceinline__ void wg_tile(int w, int BH, int ntiles, int& bh, int& rank) {
+  const int total = BH * ntiles;
+  const int per = total >> 3;
+  if ((total & 7) == 0 && per % ntiles == 0) {
+    const int hx = per / ntiles;  // heads per XCD
+    const int x = w & 7, j = w >> 3;
+    bh = x * hx + j % hx;
+    rank = j / hx;
+    return;
+  }
+  bh = w / ntiles;
+  rank = w - bh * ntiles;
+}
+
 // Mask modes, mirroring fa_mask.
 enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_LOCAL = 2 };
 

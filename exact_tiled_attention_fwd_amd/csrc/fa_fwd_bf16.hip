@@ -142,15 +142,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   const int h = lane >> 5;
   const int N = a.N;
 
-  // Workgroup -> (head, query tile). Consecutive workgroup ids land on
-  // different XCDs, so the ids are regrouped to give every XCD a contiguous
-  // run of heads (their K/V stay in that XCD's L2); within a head the query
-  // tiles with the most keys go first.
-  const int total = a.BH * a.n_qtiles;
-  int w = blockIdx.x;
-  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
-  const int bh = w / a.n_qtiles;
-  int qt = w - bh * a.n_qtiles;
+  // Workgroup -> (head, query tile); under a causal mask the query tiles
+  // with the most keys go first.
+  int bh, qt;
+  wg_tile(blockIdx.x, a.BH, a.n_qtiles, bh, qt);
   if (MASK == MASK_CAUSAL) qt = a.n_qtiles - 1 - qt;
 
   const size_t base = (size_t)bh * (size_t)N * D;
@@ -547,11 +542,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
   const int grp = wv >> 2;  // waves w and w+4 share a SIMD
   const int N = a.N;
 
-  const int total = a.BH * a.n_qtiles;
-  int w = blockIdx.x;
-  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
-  const int bh = w / a.n_qtiles;
-  int qt = w - bh * a.n_qtiles;
+  int bh, qt;
+  wg_tile(blockIdx.x, a.BH, a.n_qtiles, bh, qt);
   if (MASK == MASK_CAUSAL) qt = a.n_qtiles - 1 - qt;
 
   const size_t base = (size_t)bh * (size_t)N * D;
