@@ -26,6 +26,11 @@
 //    are bank-conflict free; the next tile's global loads are in flight
 //    while the current one is computed.
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
+//  * Two schedules: the tile kernel runs all scores of a K tile, then the
+//    softmax, then P V with the exp of the next 32-key block interleaved;
+//    the block-pipelined kernel (used at d = 64) overlaps the scores of
+//    block b+1 with the exp of block b and P V of block b with the maximum
+//    of block b+1, keeping the online-softmax state per 32-key block.
 //  * The subtracted maximum is refreshed lazily: the reference m only moves
 //    when some row's tile maximum exceeds it by more than 2^RESCALE_LOG2 in
 //    exp2 units, so most tiles skip the rescale of the accumulator (p then
@@ -102,23 +107,7 @@ __device__ __forceinline__ float sum16(const f32x16& v) {
 // the lower half (the upper half adds 4): key = 8 (r / 4) + (r % 4).
 __device__ __forceinline__ constexpr int acc_key(int r) { return 8 * (r >> 2) + (r & 3); }
 
-// Swizzle of the transposed V tile (rows = value columns, BC keys per row):
-// 16-byte chunk c of row r sits at chunk c ^ swz_vt(r). Conflict free (or
-// 2-way at 64-key rows) both for the 16-byte operand reads (32 consecutive
-// rows, one chunk) and for the staging writes (16 rows eight apart).
-template <int BC>
-__device__ __forceinline__ int swz_vt(int row) {
-  if constexpr (BC == 128) return (row ^ (row >> 4)) & 15;
-  else return ((row >> 1) ^ (row >> 4)) & 7;
-}
-
-// Key-row permutation of the QK^T A operand used with the transposed V
-// tile: swapping bits 2 and 3 of the row makes accumulator register r of a
-// lane hold key 16 (r / 8) + 8 h + r % 8, so each lane's 8 probabilities of
-// a 16-key PV step are consecutive keys.
-__device__ __forceinline__ int perm_rows(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
-
-template <int D, int QB, int NW, int BC, int MASK, bool DMA, bool VT = false>
+template <int D, int QB, int NW, int BC, int MASK>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QW = QB * 32;       // query rows per wave
@@ -194,107 +183,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   key_range<MASK>(qw0, qw0 + QW, N, a.window, wk_lo, wk_hi);
   const bool wave_live = qw0 < N;
 
-  // K/V staging. Register path: global -> VGPR -> LDS. DMA path:
-  // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS at the wave's
-  // base + 16 i, so each lane fetches the global chunk that belongs at its
-  // LDS slot under the XOR swizzle. Rows past N are clamped to row N-1:
-  // their keys are masked, so only finiteness of the data matters.
-  constexpr int CPW = DMA ? CPT : 1;  // 16-byte chunks per lane per tile (DMA)
-  u32x4 stK[DMA ? 1 : CPT], stV[DMA ? 1 : CPT];
+  // K/V staging: global_load_lds_dwordx4 writes lane i's 16 bytes to LDS at
+  // the wave's base + 16 i, so each lane fetches the global chunk that
+  // belongs at its LDS slot under the XOR swizzle. Rows past N are clamped
+  // to row N-1: their keys are masked, so only finiteness of the data matters.
   auto dma = [&](int t, int buf) {
     const int k0 = t * BC;
     char* sK = smem + buf * TILEB;
     char* sV = smem + (2 + buf) * TILEB;
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int slot = (wv * CPW + j) * 64;  // first LDS chunk of this instruction
+    for (int j = 0; j < CPT; ++j) {
+      const int slot = (wv * CPT + j) * 64;  // first LDS chunk of this instruction
       const int p = slot + lane;
       const int row = p / CPR;
       int gr = k0 + row;
       gr = gr < N ? gr : N - 1;
       const int ck = (p % CPR) ^ swz_k16<D>(row);
+      const int cv = (p % CPR) ^ swz_v16<D>(row);
       lds_dma16(K + (size_t)gr * D + ck * 8, lds_addr(sK + slot * 16));
-      if constexpr (!VT) {
-        const int cv = (p % CPR) ^ swz_v16<D>(row);
-        lds_dma16(V + (size_t)gr * D + cv * 8, lds_addr(sV + slot * 16));
-      }
-    }
-  };
-  // Transposed V staging: thread (kg, cc) loads keys KPT*kg .. +KPT-1 of the
-  // 8 value columns 8cc .. 8cc+7 (rows past N read as zero), and writes, for
-  // each of those columns, its KPT keys into row 8cc+i of the V^T tile.
-  constexpr int KPT = VT ? BC * CPR / NT : 1;
-  static_assert(!VT || (DMA && (KPT == 2 || KPT == 4)), "transposed V needs 2 or 4 keys per thread");
-  u32x4 vst[KPT];
-  auto vt_load = [&](int t) {
-    const int kg = tid / CPR, cc = tid % CPR;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int gr = t * BC + kg * KPT + j;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (gr < N) z = *(const u32x4*)(V + (size_t)gr * D + cc * 8);
-      vst[j] = z;
-    }
-  };
-  auto vt_store = [&](int buf) {
-    char* sV = smem + (2 + buf) * TILEB;
-    const int kg = tid / CPR, cc = tid % CPR;
-    const int kbyte = kg * KPT * 2;  // byte offset of these keys in a V^T row
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 8 * cc + i;
-      char* dst = sV + row * (BC * 2) + (((kbyte >> 4) ^ swz_vt<BC>(row)) << 4) + (kbyte & 15);
-      const int sh = 16 * (i & 1);
-      if constexpr (KPT == 4) {
-        u32x2 w2;
-        w2[0] = ((vst[0][i >> 1] >> sh) & 0xFFFFu) | (((vst[1][i >> 1] >> sh) & 0xFFFFu) << 16);
-        w2[1] = ((vst[2][i >> 1] >> sh) & 0xFFFFu) | (((vst[3][i >> 1] >> sh) & 0xFFFFu) << 16);
-        *(u32x2*)dst = w2;
-      } else {
-        *(unsigned*)dst = ((vst[0][i >> 1] >> sh) & 0xFFFFu) | (((vst[1][i >> 1] >> sh) & 0xFFFFu) << 16);
-      }
-    }
-  };
-  auto gload = [&](int t) {
-    const int k0 = t * BC;
-#pragma unroll
-    for (int i = 0; i < (DMA ? 0 : CPT); ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int gr = k0 + row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (gr < N) {
-        zk = *(const u32x4*)(K + (size_t)gr * D + cc * 8);
-        zv = *(const u32x4*)(V + (size_t)gr * D + cc * 8);
-      }
-      stK[i] = zk;
-      stV[i] = zv;
-    }
-  };
-  auto lstore = [&](int buf) {
-    char* sK = smem + buf * TILEB;
-    char* sV = smem + (2 + buf) * TILEB;
-#pragma unroll
-    for (int i = 0; i < (DMA ? 0 : CPT); ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      *(u32x4*)(sK + row * ROWB + ((cc ^ swz_k16<D>(row)) << 4)) = stK[i];
-      *(u32x4*)(sV + row * ROWB + ((cc ^ swz_v16<D>(row)) << 4)) = stV[i];
+      lds_dma16(V + (size_t)gr * D + cv * 8, lds_addr(sV + slot * 16));
     }
   };
 
   if (t_begin < t_end) {
-    if constexpr (DMA) {
-      dma(t_begin, 0);
-      if constexpr (VT) {
-        vt_load(t_begin);
-        vt_store(0);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS
-    } else {
-      gload(t_begin);
-      lstore(0);
-    }
+    dma(t_begin, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS
   }
   __syncthreads();
 
@@ -309,14 +222,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int buf = (t - t_begin) & 1;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
-    if (t + 1 < t_end) {
-      if constexpr (DMA) {
-        dma(t + 1, buf ^ 1);
-        if constexpr (VT) vt_load(t + 1);
-      } else {
-        gload(t + 1);
-      }
-    }
+    if (t + 1 < t_end) dma(t + 1, buf ^ 1);
     const int k0 = t * BC;
 
     // Skip tiles that hold no allowed key for any row of this wave.
@@ -335,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       auto kread = [&](int kc, int slot) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int row = kb * 32 + (VT ? perm_rows(l32) : l32);
+          const int row = kb * 32 + l32;
           kop[slot][kb] =
               *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
         }
@@ -362,14 +268,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
           const int qi = qw0 + qb * 32 + l32;
           const int q_hi_key = MASK == MASK_CAUSAL ? min(qi, N - 1)
                                : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
-          const int hoff = VT ? 8 * h : 4 * h;
+          const int hoff = 4 * h;
           const int hi_rel = q_hi_key - k0 - hoff;
           const int lo_rel = (MASK == MASK_LOCAL ? qi - a.window : 0) - k0 - hoff;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int kr = kb * 32 + (VT ? 16 * (r >> 3) + (r & 7) : acc_key(r));
+              const int kr = kb * 32 + acc_key(r);
               const bool ok =
                   (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
               sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
@@ -422,15 +328,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       // O^T += V^T P^T for one 32-key block; each V read feeds QB MFMAs.
       bf16x8 vop[2][DT];
       auto vread = [&](int kb, int u) {
-        if constexpr (VT) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int row = dt * 32 + l32;
-            const int ch = (4 * kb + 2 * u + h) ^ swz_vt<BC>(row);
-            vop[u][dt] = *(const bf16x8*)(sV + row * (BC * 2) + ch * 16);
-          }
-          return;
-        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
@@ -461,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         if (kb < KB) exp_block(kb);
         pv_mfma(kb - 1, 0);
         pv_mfma(kb - 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, VT ? 2 * DT : 4 * DT, 0);  // all V reads of the block
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DT, 0);  // all V reads of the block
         if (kb < KB) {
           __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);     // VALU while they land
 #pragma unroll
@@ -476,14 +373,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb];
     }
 
-    if constexpr (DMA) {
-      if constexpr (VT) {
-        if (t + 1 < t_end) vt_store(buf ^ 1);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
-    } else {
-      if (t + 1 < t_end) lstore(buf ^ 1);
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
     __syncthreads();
   }
 
@@ -509,20 +399,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
+// Compile-time integer tag for generic lambdas.
+template <int V>
+struct ic {
+  static constexpr int value = V;
+};
+
 // ---------------------------------------------------------------------------
-// Ping-pong schedule. The eight waves form two groups of four, one wave of
-// each group per SIMD. Every wave alternates an MFMA phase (scores of tile j
-// and P V of tile j-1) and a VALU phase (online softmax of tile j), and the
-// two groups run one phase apart, separated by workgroup barriers: while one
-// group keeps the matrix core busy, the other group's exp / max / convert
-// work runs on the vector ALU of the same SIMD.
-//
-// Global phase f: group 0 is in MFMA phase f/2 when f is even, group 1 when
-// f is odd. K_j is read in phases 2j, 2j+1 and V_j in 2j+2, 2j+3, so both
-// are double-buffered, and odd phase 2i+1 stores K_{i+1} and V_i to LDS
-// (their buffers were last read in phase 2i-1).
+// Block-pipelined variant. The online softmax runs per 32-key block (the
+// lazily refreshed reference makes any key grouping valid), and inside each
+// LDS tile every wave alternates two phases per block b:
+//   A: S(b+1) = K(b+1) Q^T on the matrix core, beside exp / row sum / bf16
+//      convert of block b on the vector ALU;
+//   B: O += P(b) V(b) on the matrix core, beside mask and row maximum of
+//      block b+1, followed by the reference check for block b+1.
+// Each stretch of matrix work thus has independent vector work next to it
+// in the same instruction stream, and only two 32-key score blocks are live.
 template <int D, int BC, int MASK>
-__global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
   constexpr int NW = 8;
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
@@ -532,14 +426,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
   constexpr int CPR = D / 8;
-  constexpr int CPW = BC * CPR / NT;  // DMA chunks per lane per tile
+  constexpr int CPW = BC * CPR / NT;  // DMA chunks per lane per tile (K or V)
   static_assert((BC * CPR) % NT == 0 && CPW >= 1, "tile chunks must divide evenly");
+  static_assert(KC % 4 == 0, "four exp pieces spread over the QK steps");
 
   __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2], V[2]
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int grp = wv >> 2;  // waves w and w+4 share a SIMD
   const int N = a.N;
 
   int bh, qt;
@@ -567,35 +461,33 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_ref = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f, mc = 0.f;
   const float c = a.scale_log2;
 
   int k_lo, k_hi;
   key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
-  const int tb = k_lo / BC;
-  const int T = (k_hi + BC - 1) / BC - tb;  // tiles of this workgroup (>= 1)
+  const int t_begin = k_lo / BC;
+  const int t_end = (k_hi + BC - 1) / BC;
   int wk_lo, wk_hi;
   key_range<MASK>(qw0, qw0 + 32, N, a.window, wk_lo, wk_hi);
   const bool wave_live = qw0 < N;
-  auto active = [&](int j) {  // tile j (relative) holds allowed keys for this wave
-    const int k0 = (tb + j) * BC;
-    return wave_live && j >= 0 && j < T && k0 < wk_hi && k0 + BC > wk_lo;
-  };
   const int q_hi_key = MASK == MASK_CAUSAL ? min(qi, N - 1)
                        : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
   const int q_lo_key = MASK == MASK_LOCAL ? qi - a.window : 0;
 
-  // direct global->LDS staging of K_j (buffer j&1) or V_j (buffer 2 + (j&1))
-  auto dma = [&](const bf16* __restrict__ src, int j, char* dst_tile, bool vrow) {
+  // direct global->LDS copy of key tile t into buffer buf (K) and 2 + buf (V)
+  auto dma = [&](int t, int buf) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int slot = (wv * CPW + i) * 64;
       const int p = slot + lane;
       const int row = p / CPR;
-      int gr = (tb + j) * BC + row;
+      int gr = t * BC + row;
       gr = gr < N ? gr : N - 1;  // keys past N are masked
-      const int cc = (p % CPR) ^ (vrow ? swz_v16<D>(row) : swz_k16<D>(row));
-      lds_dma16(src + (size_t)gr * D + cc * 8, lds_addr(dst_tile + slot * 16));
+      const int ck = (p % CPR) ^ swz_k16<D>(row);
+      const int cv = (p % CPR) ^ swz_v16<D>(row);
+      lds_dma16(K + (size_t)gr * D + ck * 8, lds_addr(smem + buf * TILEB + slot * 16));
+      lds_dma16(V + (size_t)gr * D + cv * 8, lds_addr(smem + (2 + buf) * TILEB + slot * 16));
     }
   };
 
@@ -603,135 +495,152 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
   const int tr_row = 4 * h + (s16 >> 2);
   const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
 
-  f32x16 sacc[KB];
-  bf16x8 pop[KB][2];
-
-  // MFMA phase j: scores of tile j and P V of tile j-1, operands prefetched
-  auto mfma_phase = [&](int j) {
-    const bool doqk = active(j), dopv = active(j - 1);
-    const char* sK = smem + (j & 1) * TILEB;
-    const char* sV = smem + (2 + ((j - 1) & 1)) * TILEB;
-    bf16x8 vop[2][DT];
-    auto vread = [&](int kb, int u) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
-        const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
-        const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
-        vop[u][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    if (doqk) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      bf16x8 kop[2][KB];
-      auto kread = [&](int kc, int slot) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int row = kb * 32 + l32;
-          kop[slot][kb] = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
-        }
-      };
-      kread(0, 0);
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        if (kc + 1 < KC) kread(kc + 1, (kc + 1) & 1);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc & 1][kb], qop[kc], sacc[kb], 0, 0, 0);
-        if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (dopv) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        vread(kb, 0);
-        vread(kb, 1);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[kb][u], oacc[dt], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * DT, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-  // VALU phase: online softmax of tile j (its scores are in sacc)
-  auto softmax = [&](int j) {
-    const int k0 = (tb + j) * BC;
-    if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + 32, k0, k0 + BC, a.window)) {
-      const int hi_rel = q_hi_key - k0 - 4 * h;
-      const int lo_rel = q_lo_key - k0 - 4 * h;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = kb * 32 + acc_key(r);
-          const bool ok = (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
-          sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
-        }
-    }
-    float mx = max16(sacc[0]);
-#pragma unroll
-    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, max16(sacc[kb]));
-    mx = pair_max(mx);
-    if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > RESCALE_LOG2)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
-    const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * c;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
-      ls += sum16(sacc[kb]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pop[kb][u][e] = (bf16)sacc[kb][8 * u + e];
-    }
-    l_run += ls;
-  };
-
-  // prologue: K_0 resident
-  dma(K, 0, smem, false);
+  if (t_begin < t_end) dma(t_begin, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  // Global phase f: group 0 runs MFMA phase f/2 on even f, group 1 MFMA
-  // phase (f-1)/2 on odd f; each group's VALU phase follows its MFMA phase.
-  // K_j is read in phases 2j, 2j+1 and V_j in 2j+2, 2j+3; even phase 2i
-  // starts the loads of K_{i+1} and V_i (their buffers were last read in
-  // phase 2i-1) and odd phase 2i+1 waits for them before its barrier.
-  for (int f = 0; f < 2 * T + 2; ++f) {
-    if ((f & 1) == 0) {
-      const int i = f >> 1;
-      if (i + 1 < T) dma(K, i + 1, smem + ((i + 1) & 1) * TILEB, false);
-      if (i < T) dma(V, i, smem + (2 + (i & 1)) * TILEB, true);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const char* sK = smem + buf * TILEB;
+    const char* sV = smem + (2 + buf) * TILEB;
+    if (t + 1 < t_end) dma(t + 1, buf ^ 1);
+    const int k0 = t * BC;
+
+    if (wave_live && k0 < wk_hi && k0 + BC > wk_lo) {
+      f32x16 sacc[2];
+      bf16x8 pop[2][2];
+      auto kread = [&](int kb, int kc, bf16x8& kop) {
+        const int row = kb * 32 + l32;
+        kop = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
+      };
+      auto vread = [&](int kb, int u, bf16x8 (&vop)[DT]) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
+          vop[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+      // mask of block kb (tiles this wave does not see whole)
+      auto mask_block = [&](f32x16& S, int kb) {
+        const int kb0 = k0 + kb * 32;
+        const int hi_rel = q_hi_key - kb0 - 4 * h;
+        const int lo_rel = q_lo_key - kb0 - 4 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = acc_key(r);
+          const bool ok = (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
+          S[r] = ok ? S[r] : -INFINITY;
+        }
+      };
+      auto rescale = [&](float mx) {
+        if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > RESCALE_LOG2)) {
+          const float m_new = fmaxf(m_ref, mx);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+          m_ref = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+        mc = (m_ref == -INFINITY ? 0.f : m_ref) * c;
+      };
+      // exp piece q of block scores S (registers 4q..4q+3); the last piece
+      // adds the row-sum part (to l_run, which a later rescale scales with
+      // the numerator) and writes the bf16 operand P
+      auto exp_piece = [&](f32x16& S, int q, bf16x8 (&P)[2]) {
+#pragma unroll
+        for (int r = 4 * q; r < 4 * q + 4; ++r)
+          S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -mc));
+        if (q == 3) {
+          l_run += sum16(S);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) P[u][e] = (bf16)S[8 * u + e];
+        }
+      };
+
+      // The tile body, with the per-element mask compiled in (tiles this
+      // wave does not see whole) or out (all other tiles: no branch inside).
+      auto body = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+      // block 0: scores, mask, maximum
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[0][r] = 0.f;
+      {
+        bf16x8 kop[2];
+        kread(0, 0, kop[0]);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          if (kc + 1 < KC) kread(0, kc + 1, kop[(kc + 1) & 1]);
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc & 1], qop[kc], sacc[0], 0, 0, 0);
+        }
+      }
+      if constexpr (MASKED) mask_block(sacc[0], 0);
+      rescale(pair_max(max16(sacc[0])));
+
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int P0 = kb & 1, P1 = P0 ^ 1;
+        bf16x8 vop[2][DT];
+        // ---- phase A: S(kb+1) beside exp of block kb; then the V operands
+        // of block kb are requested
+        if (kb + 1 < KB) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[P1][r] = 0.f;
+          bf16x8 kop[KC];
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) kread(kb + 1, kc, kop[kc]);
+          __builtin_amdgcn_sched_group_barrier(0x100, KC, 0);
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            sacc[P1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc], qop[kc], sacc[P1], 0, 0, 0);
+            if (kc % (KC / 4) == KC / 4 - 1) exp_piece(sacc[P0], kc / (KC / 4), pop[P0]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 28 / KC, 0);
+          }
+          // keep the exp work in this stretch (it would otherwise sink to its
+          // use in the P V step below)
+          asm volatile("" : "+v"(pop[P0][0]), "+v"(pop[P0][1]), "+v"(l_run));
+          vread(kb, 0, vop[0]);
+          vread(kb, 1, vop[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          vread(kb, 0, vop[0]);
+          vread(kb, 1, vop[1]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) exp_piece(sacc[P0], q, pop[P0]);
+        }
+        // ---- phase B: O += P(kb) V(kb) beside mask / maximum of block kb+1
+        float mx = -INFINITY;
+        {
+          if (MASKED && kb + 1 < KB) mask_block(sacc[P1], kb + 1);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[P0][u], oacc[dt], 0, 0, 0);
+          if (kb + 1 < KB) mx = pair_max(max16(sacc[P1]));
+#pragma unroll
+          for (int i = 0; i < 2 * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kb + 1 < KB) rescale(mx);
+      }
+      };
+      if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + 32, k0, k0 + BC, a.window)) body(ic<1>{});
+      else body(ic<0>{});
     }
-    if ((f & 1) == grp) {
-      mfma_phase((f - grp) >> 1);
-    } else {
-      const int js = grp == 0 ? (f - 1) >> 1 : (f >> 1) - 1;
-      if (active(js)) softmax(js);
-    }
-    if (f & 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K_{i+1}, V_i landed
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
     __syncthreads();
   }
 
@@ -753,56 +662,50 @@ __global__ __launch_bounds__(512) void fwd_bf16_pp_kernel(FwdArgs a) {
 }
 
 template <int D, int BC>
-static hipError_t launch_fwd_bf16_pp(const FwdArgs& a0, int mask, hipStream_t stream) {
+static hipError_t launch_fwd_bf16_xb(const FwdArgs& a0, int mask, hipStream_t stream) {
   FwdArgs a = a0;
   a.n_qtiles = (a.N + 255) / 256;
   dim3 grid((unsigned)(a.n_qtiles * a.BH)), block(512);
   switch (mask) {
-    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
-    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, BC, MASK_NONE>), grid, block, 0, stream, a); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_xb_kernel<D, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
+    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_xb_kernel<D, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_xb_kernel<D, BC, MASK_NONE>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
-template <int D, int QB, int NW, int BC, bool DMA = false, bool VT = false>
+template <int D, int QB, int NW, int BC>
 static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t stream) {
   FwdArgs a = a0;
   constexpr int BR = NW * QB * 32;
   a.n_qtiles = (a.N + BR - 1) / BR;
   dim3 grid((unsigned)(a.n_qtiles * a.BH)), block(NW * 64);
   switch (mask) {
-    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_CAUSAL, DMA, VT>), grid, block, 0, stream, a); break;
-    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_LOCAL, DMA, VT>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_NONE, DMA, VT>), grid, block, 0, stream, a); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
+    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_NONE>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
-// Tile configurations (NW waves of QB x 32 query rows, BC keys per tile,
-// DMA = direct global->LDS staging, VT = transposed V tile). The default was
-// picked by interleaved timing on MI355X (causal 8192 x 128, 2048 x 64 and
-// the 16384 x 128 band); the others stay selectable for tuning sweeps.
+// Kernel choice per head dimension, picked by interleaved timing on MI355X
+// (causal 8192 x 128, 4096 x 128, unmasked 2048 x 64, band 16384 x 128):
+// d = 128 uses the tile kernel with 128-key tiles, d = 64 the block-pipelined
+// kernel with 64-key tiles. cfg selects the alternatives for timing sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
     switch (cfg) {
-      case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64, true>(a, mask, stream);
-      case 2: return launch_fwd_bf16_cfg<128, 1, 8, 64, false>(a, mask, stream);
-      case 3: return launch_fwd_bf16_pp<128, 64>(a, mask, stream);
-      case 6: return launch_fwd_bf16_pp<128, 128>(a, mask, stream);
-      case 4: return launch_fwd_bf16_cfg<128, 1, 8, 64, true, true>(a, mask, stream);
-      case 5: return launch_fwd_bf16_cfg<128, 1, 4, 64, true>(a, mask, stream);
-      default: return launch_fwd_bf16_cfg<128, 1, 8, 128, true>(a, mask, stream);
+      case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64>(a, mask, stream);
+      case 2: return launch_fwd_bf16_xb<128, 128>(a, mask, stream);
+      case 3: return launch_fwd_bf16_xb<128, 64>(a, mask, stream);
+      default: return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
     }
   }
   switch (cfg) {
-    case 1: return launch_fwd_bf16_cfg<64, 1, 8, 64, true>(a, mask, stream);
-    case 2: return launch_fwd_bf16_cfg<64, 1, 8, 64, false>(a, mask, stream);
-    case 3: return launch_fwd_bf16_pp<64, 64>(a, mask, stream);
-    case 6: return launch_fwd_bf16_pp<64, 128>(a, mask, stream);
-    case 4: return launch_fwd_bf16_cfg<64, 1, 8, 128, true, true>(a, mask, stream);
-    case 5: return launch_fwd_bf16_cfg<64, 1, 4, 64, true>(a, mask, stream);
-    default: return launch_fwd_bf16_cfg<64, 1, 8, 128, true>(a, mask, stream);
+    case 1: return launch_fwd_bf16_cfg<64, 1, 8, 64>(a, mask, stream);
+    case 2: return launch_fwd_bf16_xb<64, 128>(a, mask, stream);
+    case 3: return launch_fwd_bf16_cfg<64, 1, 8, 128>(a, mask, stream);
+    default: return launch_fwd_bf16_xb<64, 64>(a, mask, stream);
   }
 }
 
