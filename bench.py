@@ -7,6 +7,11 @@ inputs already resident in device memory. The JSON line also carries the
 forward-only figure of the causal [2, 16, 8192, 128] workload, the roofline
 of the dominant kernel, and the CPU oracle timed on a bounded sample.
 
+Every timed section is preceded by 0.3 s of the same work back to back (the
+shader clock ramps up over the first tens of milliseconds after an idle
+spell), then the W warm-up steps, then exactly K timed steps between two
+device synchronisations.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-pmc DIR --copy-mib M   (HBM traffic summary, no GPU)
 """
@@ -224,6 +229,20 @@ def main():
         if have_bwd:
             bwd()
 
+    CLOCK_SETTLE_S = 0.3
+
+    def settle(fn):
+        """Run fn back to back for CLOCK_SETTLE_S seconds: the shader clock
+        ramps up over the first tens of milliseconds of load after an idle
+        spell (e.g. host-side input generation), and the W warm-up steps
+        alone are too short for that."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < CLOCK_SETTLE_S:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+
     def timed(fn, reps):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
@@ -235,6 +254,15 @@ def main():
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps  # ms
 
+    if not args.no_headline:  # headline inputs first: no idle gap between timed sections
+        hw = WORKLOADS["bf16_causal_b2h16_n8192_d128"]
+        hin = make_inputs(hw)
+        hq, hk, hv = (hin[n].to(dev) for n in ("q", "k", "v"))
+        ho = torch.empty_like(hq)
+        hl = torch.empty(hq.shape[:-1], dtype=torch.float32, device=dev)
+        del hin
+
+    settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -281,19 +309,15 @@ def main():
                    "fwd_tflops": round(fwd_flops(w) / (ms_fwd * 1e-3) / 1e12, 1),
                    "bwd_tflops": round(bwd_flops(w) / (kernels["fa_bwd"][0] * 1e-3) / 1e12, 1)
                    if have_bwd else None,
-                   "wall_s_timed": round(wall, 3)},
+                   "wall_s_timed": round(wall, 3),
+                   "clock_settle_s": CLOCK_SETTLE_S},
         "roofline": roofline,
     }
 
     if not args.no_headline:
-        hw = WORKLOADS["bf16_causal_b2h16_n8192_d128"]
-        hin = make_inputs(hw)
-        hq, hk, hv = (hin[n].to(dev) for n in ("q", "k", "v"))
-        ho = torch.empty_like(hq)
-        hl = torch.empty(hq.shape[:-1], dtype=torch.float32, device=dev)
-
         def hfwd():
             fa.fa_fwd(hq, hk, hv, ho, hl, hw.scale, hw.mask, hw.window, stream)
+        settle(hfwd)
         for _ in range(args.warmup):
             hfwd()
         hms = timed(hfwd, args.steps)
