@@ -14,6 +14,7 @@ device synchronisations.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-pmc DIR --copy-mib M   (HBM traffic summary, no GPU)
+       python bench.py --sweep        (N = 2k..16k sweep, markdown table on stdout)
 """
 import argparse
 import csv
@@ -23,8 +24,10 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -183,6 +186,9 @@ def main():
                     help="print the HBM traffic summary of the rocprofv3 counter CSVs in DIR")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size of the calibration copy used with --summarize-pmc")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
+                         "d in {64, 128}, mask in {none, causal}; prints a markdown table")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc, args.copy_mib))
@@ -204,6 +210,9 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(torch, dev, args)
+        return
+    if args.sweep:
+        sweep(torch, fa, dev, args)
         return
 
     have_bwd = not args.fwd_only
@@ -262,6 +271,7 @@ def main():
         hl = torch.empty(hq.shape[:-1], dtype=torch.float32, device=dev)
         del hin
 
+    peaks = measured_peaks(torch, fa, dev, stream)
     settle(step)
     for _ in range(args.warmup):
         step()
@@ -286,6 +296,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "traffic_unit": "bytes per call", "traffic_source": traffic_src,
                 "algorithmic_bytes_per_launch": by_dom, "kernel": dom,
+                "peak_measured": round(peaks["mfma_bf16_tflops"], 1),
+                "frac_of_measured": round(achieved / peaks["mfma_bf16_tflops"], 4),
                 "algorithmic_flop_per_launch": fl_dom,
                 "avg_launch_us": round(ms_dom * 1e3, 2)}
 
@@ -312,6 +324,7 @@ def main():
                    "wall_s_timed": round(wall, 3),
                    "clock_settle_s": CLOCK_SETTLE_S},
         "roofline": roofline,
+        "probes": {k_: round(v_, 1) for k_, v_ in peaks.items()},
     }
 
     if not args.no_headline:
@@ -332,6 +345,89 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inp, have_bwd)
 
     print(json.dumps(out), flush=True)
+
+
+def measured_peaks(torch, fa, dev, stream):
+    """The library's roofline probes, best of three runs each: sustained
+    bf16 MFMA TFLOP/s of register-operand MFMAs on every compute unit, and
+    HBM GB/s of a 1 GiB device copy (read + write)."""
+    mf = max(fa.fa_probe_mfma_bf16(100000, stream) for _ in range(3))
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cp = max(fa.fa_probe_copy(src, dst, 10, stream) for _ in range(3))
+    del src, dst
+    return {"mfma_bf16_tflops": mf, "hbm_copy_gbs": cp}
+
+
+def sweep(torch, fa, dev, args):
+    """fa_fwd and fa_bwd over N = 2048..16384 with B = 32768/N and H = 16,
+    d in {64, 128}, mask in {none, causal}. Inputs are N(0,1) bf16 drawn on
+    the device (seeded; timing only, no parity). Each entry point first runs
+    back to back for 0.1 s (clock settle); 'warm' is the mean of K launches
+    back to back, 'flushed' the median of K launches each preceded by a
+    512 MiB device write that evicts L2 and the 256 MB MALL."""
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(args.steps, 5)
+    peaks = measured_peaks(torch, fa, dev, stream)
+    print(f"Measured ceilings: bf16 MFMA {peaks['mfma_bf16_tflops']:.0f} TFLOP/s, "
+          f"HBM copy {peaks['hbm_copy_gbs']:.0f} GB/s.\n")
+    print("| d | mask | N | B | unit | flushed µs | warm µs | TFLOP/s (flushed) | % of 2516.6 | "
+          "% of measured | HBM GB/s (algorithmic bytes, flushed) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+
+    def one(fn):
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        fn()
+        e_.record(stream)
+        e_.synchronize()
+        return s_.elapsed_time(e_)
+
+    for d in (64, 128):
+        for mask in ("none", "causal"):
+            for N in (2048, 4096, 8192, 16384):
+                B, H = 32768 // N, 16
+                g = torch.Generator(device=dev).manual_seed(7919 * N + d)
+                q, k, v, do = (torch.randn(B, H, N, d, generator=g, device=dev).to(torch.bfloat16)
+                               for _ in range(4))
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+                ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d, q.dtype), dtype=torch.uint8,
+                                 device=dev)
+                scale = d ** -0.5
+                w = types.SimpleNamespace(shape=(B, H, N, d), mask=mask, window=0, dtype="bf16")
+                units = (("fa_fwd", lambda: fa.fa_fwd(q, k, v, o, lse, scale, mask, 0, stream),
+                          fwd_flops(w), fwd_bytes(w)),
+                         ("fa_bwd", lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale,
+                                                      mask, 0, stream),
+                          bwd_flops(w), bwd_bytes(w)))
+                units[0][1]()  # O and LSE for the backward
+                for name, fn, flops, nbytes in units:
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    while time.perf_counter() - t0 < 0.1:
+                        fn()
+                        torch.cuda.synchronize()
+                    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s_.record(stream)
+                    for _ in range(reps):
+                        fn()
+                    e_.record(stream)
+                    e_.synchronize()
+                    warm = s_.elapsed_time(e_) / reps
+                    fl = []
+                    for i in range(reps):
+                        scratch.fill_(i & 255)
+                        fl.append(one(fn))
+                    ms = statistics.median(fl)
+                    tf = flops / (ms * 1e-3) / 1e12
+                    print(f"| {d} | {mask} | {N} | {B} | {name} | {ms * 1e3:.1f} | {warm * 1e3:.1f} | "
+                          f"{tf:.1f} | {100 * tf / PEAK_BF16_TFLOPS:.1f} | "
+                          f"{100 * tf / peaks['mfma_bf16_tflops']:.1f} | "
+                          f"{nbytes / (ms * 1e-3) / 1e9:.0f} |", flush=True)
+                del q, k, v, do, o, lse, dq, dk, dv, ws
 
 
 def copy_probe(torch, dev, args):

@@ -2,18 +2,19 @@
 
 The computation runs in hand-written HIP kernels behind the C ABI of
 include/fa.h (libfa.so). This package is the thin Python side: the ctypes
-binding (same names as the C entry points) plus two convenience wrappers
-that allocate outputs with torch.
+binding (same names as the C entry points of include/fa.h and the roofline
+probes of include/fa_probe.h) plus two convenience wrappers that allocate
+outputs with torch.
 """
 import math
 
 import torch
 
-from ._native import (FAError, fa_bwd, fa_bwd_workspace_bytes, fa_fwd, fa_status_string,
-                      load)
+from ._native import (FAError, fa_bwd, fa_bwd_workspace_bytes, fa_fwd, fa_probe_copy,
+                      fa_probe_mfma_bf16, fa_status_string, load)
 
 __all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "load",
-           "attention_fwd", "attention_bwd"]
+           "fa_probe_mfma_bf16", "fa_probe_copy", "attention_fwd", "attention_bwd"]
 
 
 def _default_scale(d):

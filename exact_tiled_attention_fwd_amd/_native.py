@@ -49,6 +49,11 @@ def load():
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.fa_probe_mfma_bf16.argtypes = [i, vp, dp]
+    lib.fa_probe_mfma_bf16.restype = i
+    lib.fa_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, i, vp, dp]
+    lib.fa_probe_copy.restype = i
     _lib = lib
     return lib
 
@@ -89,6 +94,12 @@ def _check(name, t, ref=None, dtype=None, shape=None):
 def _stream(t, stream):
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
@@ -134,3 +145,27 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, windo
                        _mask_code(mask), int(window), _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_bwd")
+
+
+def fa_probe_mfma_bf16(iters, stream=None) -> float:
+    """Call fa_probe_mfma_bf16 (waits for the device): sustained bf16 MFMA
+    TFLOP/s of a full-device grid of register-operand MFMAs."""
+    out = ctypes.c_double(0.0)
+    st = load().fa_probe_mfma_bf16(int(iters), _stream_handle(stream), ctypes.byref(out))
+    if st != 0:
+        raise FAError(st, "fa_probe_mfma_bf16")
+    return out.value
+
+
+def fa_probe_copy(src, dst, reps, stream=None) -> float:
+    """Call fa_probe_copy (waits for the device) on two equally sized uint8
+    GPU tensors: GB/s of bytes read plus bytes written."""
+    _check("src", src)
+    _check("dst", dst, src, src.dtype, src.shape)
+    nbytes = src.numel() * src.element_size()
+    out = ctypes.c_double(0.0)
+    st = load().fa_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(reps),
+                              _stream(src, stream), ctypes.byref(out))
+    if st != 0:
+        raise FAError(st, "fa_probe_copy")
+    return out.value

@@ -80,3 +80,18 @@ def test_bwd_argument_errors(lib):
     assert bwd(mask=2, window=-2) == 5
     assert bwd(scale=float("nan")) == 6
     assert bwd(d=100) == 4
+
+
+def test_probe_argument_errors(lib):
+    out = ctypes.c_double(0.0)
+    ref = ctypes.byref(out)
+    assert lib.fa_probe_mfma_bf16(100, None, None) == 1          # FA_ERR_NULL
+    assert lib.fa_probe_mfma_bf16(0, None, ref) == 2             # FA_ERR_SHAPE
+    assert lib.fa_probe_mfma_bf16(1 << 25, None, ref) == 2
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    assert lib.fa_probe_copy(None, b, 256, 1, None, ref) == 1
+    assert lib.fa_probe_copy(a, b, 0, 1, None, ref) == 2
+    assert lib.fa_probe_copy(a, b, 256, 0, None, ref) == 2
+    assert lib.fa_probe_copy(a, b, 250, 1, None, ref) == 7          # size not a multiple of 16
+    assert lib.fa_probe_copy(ctypes.c_void_p(0x100008), b, 256, 1, None, ref) == 7
+    assert lib.fa_probe_copy(a, ctypes.c_void_p(0x100080), 256, 1, None, ref) == 10  # overlap
