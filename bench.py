@@ -15,6 +15,7 @@ device synchronisations.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-pmc DIR --copy-mib M   (HBM traffic summary, no GPU)
        python bench.py --sweep        (N = 2k..16k sweep, markdown table on stdout)
+       python bench.py --gemm-ref     (vendor bf16 GEMM rate, for context)
 """
 import argparse
 import csv
@@ -186,6 +187,8 @@ def main():
                     help="print the HBM traffic summary of the rocprofv3 counter CSVs in DIR")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size of the calibration copy used with --summarize-pmc")
+    ap.add_argument("--gemm-ref", action="store_true",
+                    help="time torch.matmul (hipBLASLt) on bf16 8192^3 and 4096^3 for context")
     ap.add_argument("--sweep", action="store_true",
                     help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
@@ -213,6 +216,9 @@ def main():
         return
     if args.sweep:
         sweep(torch, fa, dev, args)
+        return
+    if args.gemm_ref:
+        gemm_ref(torch, dev)
         return
 
     have_bwd = not args.fwd_only
@@ -428,6 +434,30 @@ def sweep(torch, fa, dev, args):
                           f"{100 * tf / peaks['mfma_bf16_tflops']:.1f} | "
                           f"{nbytes / (ms * 1e-3) / 1e9:.0f} |", flush=True)
                 del q, k, v, do, o, lse, dq, dk, dv, ws
+
+
+def gemm_ref(torch, dev):
+    """The vendor library's dense bf16 GEMM (torch.matmul -> hipBLASLt) on
+    square shapes: context for what a plain contraction sustains on this card."""
+    out = {}
+    for n in (4096, 8192):
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:  # clock settle
+            a @ b
+            torch.cuda.synchronize()
+        reps = 20
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        for _ in range(reps):
+            a @ b
+        e_.record()
+        e_.synchronize()
+        ms = s_.elapsed_time(e_) / reps
+        out[f"bf16_gemm_{n}^3_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    print(json.dumps(out), flush=True)
 
 
 def copy_probe(torch, dev, args):
