@@ -16,6 +16,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-pmc DIR --copy-mib M   (HBM traffic summary, no GPU)
        python bench.py --sweep        (N = 2k..16k sweep, markdown table on stdout)
        python bench.py --gemm-ref     (vendor bf16 GEMM rate, for context)
+       python bench.py --std-sweep [--std-n N] [--no-settle]
+                                      (fused fa_fwd vs standard fa_fwd_standard, N = 1k..16k)
+       python bench.py --summarize-std DIR   (their HBM bytes from per-N counter passes, no GPU)
 """
 import argparse
 import csv
@@ -189,12 +192,24 @@ def main():
                     help="size of the calibration copy used with --summarize-pmc")
     ap.add_argument("--gemm-ref", action="store_true",
                     help="time torch.matmul (hipBLASLt) on bf16 8192^3 and 4096^3 for context")
+    ap.add_argument("--std-sweep", action="store_true",
+                    help="fused fa_fwd vs the standard unfused fa_fwd_standard, bf16 [1,16,N,64], "
+                         "no mask, N = 1024..16384; prints a markdown table")
+    ap.add_argument("--std-n", type=int, default=0, help="only this N in --std-sweep")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="--std-sweep: skip the clock settle and the warm launches "
+                         "(counter passes: only the flushed launches run)")
+    ap.add_argument("--summarize-std", default=None,
+                    help="HBM bytes of fused vs standard from the per-N counter CSVs in DIR")
     ap.add_argument("--sweep", action="store_true",
                     help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc, args.copy_mib))
+        return
+    if args.summarize_std:
+        print(summarize_std(args.summarize_std, args.copy_mib))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
@@ -219,6 +234,9 @@ def main():
         return
     if args.gemm_ref:
         gemm_ref(torch, dev)
+        return
+    if args.std_sweep:
+        std_sweep(torch, fa, dev, args)
         return
 
     have_bwd = not args.fwd_only
@@ -434,6 +452,115 @@ def sweep(torch, fa, dev, args):
                           f"{100 * tf / peaks['mfma_bf16_tflops']:.1f} | "
                           f"{nbytes / (ms * 1e-3) / 1e9:.0f} |", flush=True)
                 del q, k, v, do, o, lse, dq, dk, dv, ws
+
+
+STD_NS = (1024, 2048, 4096, 8192, 16384)
+
+
+def std_bytes(N, B=1, H=16, d=64):
+    """Algorithmic HBM bytes of the two forwards at bf16 [B,H,N,d]: the fused
+    one reads Q, K, V and writes O, LSE; the standard one also writes S
+    (float32) and reads it back, writes P (bf16) and reads it back."""
+    fused = 4 * B * H * N * d * 2 + B * H * N * 4
+    return fused, fused + B * H * N * N * (4 + 4 + 2 + 2)
+
+
+def std_sweep(torch, fa, dev, args):
+    """Time the fused forward and the standard (unfused) one on the notes'
+    setting (d = 64, no mask), B = 1, H = 16, N = 1024..16384 (or --std-n).
+    'flushed': median of launches each preceded by a 512 MiB device write
+    (evicts L2 and the 256 MB MALL); 'warm': mean of launches back to back
+    after a 0.1 s clock settle."""
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(args.steps, 3)
+    print("| N | fused flushed µs | fused warm µs | standard flushed µs | standard warm µs | "
+          "standard / fused (flushed) | fused bytes (MB) | standard bytes (MB) | "
+          "standard workspace (GB) |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    B, H, d = 1, 16, 64
+    for N in ([args.std_n] if args.std_n else STD_NS):
+        g = torch.Generator(device=dev).manual_seed(104729 + N)
+        q, k, v = (torch.randn(B, H, N, d, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        wsb = fa.fa_fwd_standard_workspace_bytes(B, H, N, d, q.dtype)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        units = (lambda: fa.fa_fwd(q, k, v, o, lse, 0.125, "none", 0, stream),
+                 lambda: fa.fa_fwd_standard(q, k, v, o, lse, ws, 0.125, "none", 0, stream))
+        res = []
+        for fn in units:
+            warm = float("nan")
+            if not args.no_settle:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < 0.1:
+                    fn()
+                    torch.cuda.synchronize()
+                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s_.record(stream)
+                for _ in range(reps):
+                    fn()
+                e_.record(stream)
+                e_.synchronize()
+                warm = s_.elapsed_time(e_) / reps
+            fl = []
+            for i in range(reps):
+                scratch.fill_(i & 255)
+                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s_.record(stream)
+                fn()
+                e_.record(stream)
+                e_.synchronize()
+                fl.append(s_.elapsed_time(e_))
+            res.append((statistics.median(fl), warm))
+        fb, sb = std_bytes(N, B, H, d)
+        (ff, fw), (sf, sw) = res
+        print(f"| {N} | {ff * 1e3:.1f} | {fw * 1e3:.1f} | {sf * 1e3:.1f} | {sw * 1e3:.1f} | "
+              f"{sf / ff:.2f} | {fb / 1e6:.1f} | {sb / 1e6:.1f} | {wsb / 1e9:.2f} |", flush=True)
+        del q, k, v, o, lse, ws
+
+
+def summarize_std(d, copy_mib):
+    """Measured HBM bytes per call of the fused and the standard forward for
+    each N whose counter CSVs are in d (fetch_N<n>_*, write_N<n>_*, plus the
+    copy calibration copy_fetch*, copy_write*), against the algorithmic
+    bytes of std_bytes()."""
+    one = lambda pat: sorted(glob.glob(os.path.join(d, pat)))[0]
+    cf = _pmc_per_dispatch(one("copy_fetch*_counter_collection.csv"), "FETCH_SIZE")
+    cw = _pmc_per_dispatch(one("copy_write*_counter_collection.csv"), "WRITE_SIZE")
+    ck = [n for n in cf if "copy" in n.lower()][0]
+    nbytes = copy_mib * (1 << 20)
+    f_fetch, f_write = nbytes / (cf[ck] * 1024.0), nbytes / (cw[ck] * 1024.0)
+    lines = ["| N | kernel | read MB | written MB |", "|---|---|---|---|"]
+    totals = []
+    for N in STD_NS:
+        fp = glob.glob(os.path.join(d, f"fetch_N{N}_counter_collection.csv"))
+        wp = glob.glob(os.path.join(d, f"write_N{N}_counter_collection.csv"))
+        if not fp or not wp:
+            continue
+        fe, wr = _pmc_per_dispatch(fp[0], "FETCH_SIZE"), _pmc_per_dispatch(wp[0], "WRITE_SIZE")
+        sums = {"fused": [0.0, 0.0], "standard": [0.0, 0.0]}
+        for name in sorted(fe):
+            unit = "standard" if "std_" in name else "fused" if "fwd_bf16" in name else None
+            if unit is None:
+                continue
+            rb, wb = fe[name] * 1024.0 * f_fetch, wr.get(name, 0.0) * 1024.0 * f_write
+            sums[unit][0] += rb
+            sums[unit][1] += wb
+            lines.append(f"| {N} | `{re.sub(r'[(<].*', '', name)}` | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        totals.append((N, sums))
+    lines += ["", "| N | fused read+write MB (algorithmic) | standard read+write MB (algorithmic) | "
+              "standard / fused bytes |", "|---|---|---|---|"]
+    for N, sums in totals:
+        fb, sb = std_bytes(N)
+        fm, sm = sum(sums["fused"]), sum(sums["standard"])
+        lines.append(f"| {N} | {fm / 1e6:.1f} ({fb / 1e6:.1f}) | {sm / 1e6:.1f} ({sb / 1e6:.1f}) | "
+                     f"{sm / fm:.1f} |")
+    lines += ["", f"Calibration: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f} "
+              f"(a {copy_mib} MiB copy through `{ck}`)."]
+    return "\n".join(lines)
 
 
 def gemm_ref(torch, dev):

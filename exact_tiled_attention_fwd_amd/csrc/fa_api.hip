@@ -131,4 +131,63 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Standard (unfused) attention: workspace = S (float32, rows padded to 4)
+// then P (bf16, rows padded to 8), each region 256-byte aligned.
+static bool std_layout(int B, int H, int N, size_t& s_bytes, size_t& total) {
+  const size_t bh = (size_t)B * H, lds = ((size_t)N + 3) & ~(size_t)3, ldp = ((size_t)N + 7) & ~(size_t)7;
+  const long double need = (long double)bh * N * (lds * 4.0L + ldp * 2.0L) + 512.0L;
+  if (need > 1.0e15L) return false;  // far beyond any device memory
+  s_bytes = (bh * N * lds * 4 + 255) & ~(size_t)255;
+  total = s_bytes + ((bh * N * ldp * 2 + 255) & ~(size_t)255);
+  return true;
+}
+
+size_t fa_fwd_standard_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
+  if (dtype != FA_BF16) return 0;
+  if (check_problem(B, H, N, d, dtype, 1.0f, FA_MASK_NONE, 0) != FA_OK) return 0;
+  size_t sb, total;
+  if (!std_layout(B, H, N, sb, total)) return 0;
+  return total;
+}
+
+fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                          fa_dtype dtype, float scale, fa_mask mask, int window, void* stream) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if ((int64_t)B * H * N > kI32Max) return FA_ERR_SHAPE;  // one softmax workgroup per row
+  size_t sb, total;
+  if (!std_layout(B, H, N, sb, total)) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < total) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins)
+    if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb) || overlap(workspace, total, in, tb))
+      return FA_ERR_ALIAS;
+  if (overlap(o, tb, lse, lb) || overlap(workspace, total, o, tb) || overlap(workspace, total, lse, lb))
+    return FA_ERR_ALIAS;
+  fa::StdArgs a;
+  a.q = (const bf16*)q;
+  a.k = (const bf16*)k;
+  a.v = (const bf16*)v;
+  a.o = (bf16*)o;
+  a.lse = lse;
+  a.s = (float*)workspace;
+  a.p = (bf16*)((char*)workspace + sb);
+  a.BH = B * H;
+  a.N = N;
+  a.lds = (N + 3) & ~3;
+  a.ldp = (N + 7) & ~7;
+  a.window = mask == FA_MASK_LOCAL ? window : 0;
+  a.scale = scale;
+  const hipError_t e = fa::launch_std_bf16(a, d, (int)mask, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"

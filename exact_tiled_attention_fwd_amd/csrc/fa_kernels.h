@@ -34,8 +34,26 @@ struct FwdF32Args {
   float scale;
 };
 
+// Standard (unfused) attention: S, P and the LSE through device memory.
+struct StdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  float* s;    // workspace: [BH][N][lds] float32 scaled, masked logits
+  bf16* p;     // workspace: [BH][N][ldp] bf16 probabilities (zero padded)
+  int BH;
+  int N;
+  int lds;     // N rounded up to 4
+  int ldp;     // N rounded up to 8
+  int window;
+  float scale;  // signed scale as given
+};
+
 // cfg selects a tile configuration (0 = default); tuning only.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream);
+hipError_t launch_std_bf16(const StdArgs& a, int d, int mask, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdF32Args& a, int mask, hipStream_t stream);
 
 }  // namespace fa

@@ -1,0 +1,252 @@
+// Standard (unfused) attention, bf16 storage, for comparison with the fused
+// forward. The three steps of the notes' "The Standard Attention Problem"
+// each make a round trip through device memory, as that page's "Memory
+// Hierarchy" section counts them:
+//   1. S = scale Q K^T, float32, every (query, key) pair; masked pairs -inf;
+//   2. row softmax: m_i, l_i, LSE_i = m_i + ln l_i, and P = exp(S - m) / l
+//      written as bf16;
+//   3. O = P V.
+// Workspace layout (fa_fwd_standard_workspace_bytes): S as [BH][N][lds]
+// float32 with lds = N rounded up to 4, then P as [BH][N][ldp] bf16 with
+// ldp = N rounded up to 8 (16-byte aligned rows).
+#include "fa_common.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <int D>
+__device__ __forceinline__ int swz_std(int row) {  // 16-byte chunk swizzle of K/V rows
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int swz_std_v(int row) {  // V rows read transposed
+  if constexpr (D == 128) return (row & 3) << 2;
+  else return ((row >> 1) & 1) << 2;
+}
+
+// ---- step 1: S = scale Q K^T. Workgroup: 256 queries (8 waves x 32) x 128
+// keys. S = Q K^T with Q as the A operand puts the key on the lane, so each
+// accumulator register of a half-wave is 32 consecutive keys of one query
+// row: 128-byte coalesced stores.
+template <int D, int MASK>
+__global__ __launch_bounds__(512) void std_scores_kernel(StdArgs a) {
+  constexpr int BC = 128, KC = D / 16, KB = BC / 32, ROWB = D * 2, CPR = D / 8;
+  constexpr int CPT = BC * CPR / 512;
+  __shared__ __attribute__((aligned(16))) char sK[BC * ROWB];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int n_kt = (N + BC - 1) / BC, n_qt = (N + 255) / 256;
+  int w = blockIdx.x;
+  const int kt = w % n_kt;
+  w /= n_kt;
+  const int qt = w % n_qt;
+  const int bh = w / n_qt;
+  const size_t base = (size_t)bh * N * D;
+  const int k0 = kt * BC, q0 = qt * 256 + wv * 32;
+
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int slot = (wv * CPT + j) * 64;
+    const int p = slot + lane;
+    const int row = p / CPR;
+    int gr = k0 + row;
+    gr = gr < N ? gr : N - 1;
+    lds_dma16(a.k + base + (size_t)gr * D + ((p % CPR) ^ swz_std<D>(row)) * 8, lds_addr(sK + slot * 16));
+  }
+  bf16x8 qop[KC];
+  const int qi = q0 + l32;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < N) x = *(const u32x4*)(a.q + base + (size_t)qi * D + kc * 16 + h * 8);
+    qop[kc] = __builtin_bit_cast(bf16x8, x);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K tile in LDS
+  __syncthreads();
+  if (q0 >= N) return;
+
+  float* S = a.s + (size_t)bh * N * a.lds;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int row = kb * 32 + l32;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const bf16x8 kop = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_std<D>(row)) << 4));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[kc], kop, acc, 0, 0, 0);
+    }
+    const int key = k0 + kb * 32 + l32;
+    if (key < N) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (i < N) {
+          const float z = allowed<MASK>(i, key, a.window) ? a.scale * acc[r] : -INFINITY;
+          S[(size_t)i * a.lds + key] = z;
+        }
+      }
+    }
+  }
+}
+
+// ---- step 2: row softmax, one workgroup of 256 threads per row: one pass
+// for the maximum and the sum (online, per thread, then merged), a second
+// pass writing P = exp(z - m) / l in bf16.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  l = l * __expf(m - mn) + l2 * __expf(m2 - mn);
+  m = mn;
+}
+
+__global__ __launch_bounds__(256) void std_softmax_kernel(StdArgs a) {
+  __shared__ float sm[4], sl[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t row = blockIdx.x;  // bh * N + i
+  const int N = a.N;
+  const float* z = a.s + row * a.lds;
+  float m = -INFINITY, l = 0.f;
+  for (int j = tid; j < N; j += 256) {
+    const float x = z[j];
+    if (x > m) {
+      l = (m == -INFINITY ? 0.f : l * __expf(m - x)) + 1.f;
+      m = x;
+    } else if (x != -INFINITY) {
+      l += __expf(x - m);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    merge_ml(m, l, m2, l2);
+  }
+  if (lane == 0) {
+    sm[wv] = m;
+    sl[wv] = l;
+  }
+  __syncthreads();
+  m = sm[0];
+  l = sl[0];
+#pragma unroll
+  for (int w2 = 1; w2 < 4; ++w2) merge_ml(m, l, sm[w2], sl[w2]);
+  const float inv = 1.f / l;
+  bf16* p = a.p + row * a.ldp;
+  for (int j = tid; j < a.ldp; j += 256) p[j] = (bf16)(j < N ? __expf(z[j] - m) * inv : 0.f);
+  if (tid == 0) a.lse[row] = m + logf(l);
+}
+
+// ---- step 3: O = P V. Workgroup: 256 queries (8 waves x 32); V tiles of 64
+// keys through double-buffered LDS (direct loads), read transposed as the A
+// operand of O^T = V^T P^T; P rows come from memory as the B operand, each
+// lane taking the 8 keys of one query that match the transposed V read
+// (keys 16u + 4h + {0..3} and 16u + 8 + 4h + {0..3} of step u).
+template <int D>
+__global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
+  constexpr int BC = 64, DT = D / 32, KB = BC / 32, ROWB = D * 2, TILEB = BC * ROWB, CPR = D / 8;
+  constexpr int CPT = BC * CPR / 512;
+  __shared__ __attribute__((aligned(16))) char sV[2 * TILEB];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int n_qt = (N + 255) / 256;
+  const int bh = blockIdx.x / n_qt, qt = blockIdx.x % n_qt;
+  const size_t base = (size_t)bh * N * D;
+  const int qi = qt * 256 + wv * 32 + l32;
+  const bf16* P = a.p + ((size_t)bh * N + (qi < N ? qi : N - 1)) * a.ldp;
+  const int n_tiles = (N + BC - 1) / BC;
+
+  auto dma = [&](int t, int buf) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int slot = (wv * CPT + j) * 64;
+      const int p = slot + lane;
+      const int row = p / CPR;
+      int gr = t * BC + row;
+      gr = gr < N ? gr : N - 1;  // P is 0 for keys past N
+      lds_dma16(a.v + base + (size_t)gr * D + ((p % CPR) ^ swz_std_v<D>(row)) * 8,
+                lds_addr(sV + buf * TILEB + slot * 16));
+    }
+  };
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+
+  dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) dma(t + 1, buf ^ 1);
+    const char* sVb = sV + buf * TILEB;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = t * BC + kb * 32 + 16 * u + 4 * h;  // first key of this lane's two groups
+        // rows hold ldp (a multiple of 8) entries, zero past N; key is a
+        // multiple of 4, so each group of 4 is either inside the row or past it
+        u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+        if (key < a.ldp) lo = *(const u32x2*)(P + key);
+        if (key + 8 < a.ldp) hi = *(const u32x2*)(P + key + 8);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_std_v<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_std_v<D>(rhi) << 1)) * 8;
+          const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sVb + rlo * ROWB + clo));
+          const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sVb + rhi * ROWB + chi));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (qi < N) {
+    bf16* O = a.o + base + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)oacc[dt][4 * r4 + e];
+        *(bf16x4*)(O + dt * 32 + 8 * r4 + 4 * h) = y;
+      }
+  }
+}
+
+template <int D, int MASK>
+static hipError_t launch_std_mask(const StdArgs& a, hipStream_t stream) {
+  const long n_kt = (a.N + 127) / 128, n_qt = (a.N + 255) / 256;
+  hipLaunchKernelGGL((std_scores_kernel<D, MASK>), dim3((unsigned)(n_kt * n_qt * a.BH)), dim3(512), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(std_softmax_kernel, dim3((unsigned)((long)a.BH * a.N)), dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((std_pv_kernel<D>), dim3((unsigned)(n_qt * a.BH)), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_std_bf16(const StdArgs& a, int d, int mask, hipStream_t stream) {
+  if (d == 128) {
+    if (mask == MASK_CAUSAL) return launch_std_mask<128, MASK_CAUSAL>(a, stream);
+    if (mask == MASK_LOCAL) return launch_std_mask<128, MASK_LOCAL>(a, stream);
+    return launch_std_mask<128, MASK_NONE>(a, stream);
+  }
+  if (mask == MASK_CAUSAL) return launch_std_mask<64, MASK_CAUSAL>(a, stream);
+  if (mask == MASK_LOCAL) return launch_std_mask<64, MASK_LOCAL>(a, stream);
+  return launch_std_mask<64, MASK_NONE>(a, stream);
+}
+
+}  // namespace fa

@@ -103,6 +103,36 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int H, int N, int d, fa_dtype dtype,
                  float scale, fa_mask mask, int window, void* stream);
 
+/*
+ * Bytes of device workspace fa_fwd_standard needs: the scores S (float32,
+ * B*H*N rows of N rounded up to 4) and the probabilities P (bf16, rows of N
+ * rounded up to 8), each region rounded up to 256 bytes. O(B*H*N^2): at
+ * [1,16,16384,*] this is 25.8 GB. Returns 0 for an invalid problem or a
+ * dtype other than FA_BF16.
+ */
+size_t fa_fwd_standard_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Standard (unfused) attention, the baseline fa_fwd is measured against: the
+ * three steps of the notes' "The Standard Attention Problem" (scores
+ * S = scale Q K^T, row softmax P, O = P V), each making a round trip through
+ * device memory, which is the traffic the notes' "Memory Hierarchy" section
+ * counts. Same O and LSE contract as fa_fwd. Every (query, key) pair is
+ * computed; masked pairs get score -inf and probability 0. P is normalized
+ * before it is rounded to bf16 and multiplied by V.
+ *   q, k, v, o, lse : as fa_fwd; dtype must be FA_BF16 (d in {64, 128}).
+ *   workspace       : device buffer of at least
+ *                     fa_fwd_standard_workspace_bytes(...) bytes, owned by the
+ *                     caller, 16-byte aligned, not overlapping any tensor;
+ *                     contents ignored on entry and undefined on return.
+ * Errors: as fa_fwd; FA_ERR_DTYPE for FA_F32; FA_ERR_WORKSPACE when the
+ * workspace is missing or too small; FA_ERR_SHAPE when B*H*N > 2^31-1.
+ */
+fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int H, int N, int d, fa_dtype dtype,
+                          float scale, fa_mask mask, int window, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);
 

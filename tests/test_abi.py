@@ -95,3 +95,23 @@ def test_probe_argument_errors(lib):
     assert lib.fa_probe_copy(a, b, 250, 1, None, ref) == 7          # size not a multiple of 16
     assert lib.fa_probe_copy(ctypes.c_void_p(0x100008), b, 256, 1, None, ref) == 7
     assert lib.fa_probe_copy(a, ctypes.c_void_p(0x100080), 256, 1, None, ref) == 10  # overlap
+
+
+def test_standard_workspace_and_errors(lib):
+    n = 300
+    want = (((1 * 2 * n * ((n + 3) // 4 * 4) * 4) + 255) // 256 * 256
+            + ((1 * 2 * n * ((n + 7) // 8 * 8) * 2) + 255) // 256 * 256)
+    assert lib.fa_fwd_standard_workspace_bytes(1, 2, n, 128, 1) == want
+    assert lib.fa_fwd_standard_workspace_bytes(1, 2, n, 128, 0) == 0   # bf16 only
+    assert lib.fa_fwd_standard_workspace_bytes(1, 2, 0, 128, 1) == 0
+    ws = ctypes.c_void_p(0x4000000)
+    def call(ws=ws, wb=1 << 40, dtype=1, d=64, N=8, q=FAKE):
+        return lib.fa_fwd_standard(q, FAKE, FAKE, ctypes.c_void_p(0x200000),
+                                   ctypes.c_void_p(0x900000), ws, wb, 1, 1, N, d, dtype, 0.125,
+                                   0, 0, None)
+    assert call(q=None) == 1
+    assert call(dtype=0) == 3                 # float32 has no standard path
+    assert call(d=96) == 4
+    assert call(ws=None) == 8 and call(wb=16) == 8
+    assert call(ws=ctypes.c_void_p(0x4000008)) == 7
+    assert call(ws=ctypes.c_void_p(0x100000)) == 10   # workspace overlaps q
