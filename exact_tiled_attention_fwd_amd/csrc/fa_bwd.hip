@@ -280,7 +280,7 @@ __device__ __forceinline__ int swz_rows(int row) {  // 16-byte chunk swizzle for
 }
 
 template <int D, int NW, int BRQ, int MASK>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
   constexpr int BC = NW * 32;       // keys per workgroup (32 per wave)
   constexpr int KC = D / 16;
   constexpr int DT = D / 32;
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
 // the B operand of dQ^T += K^T dS^T (K read transposed). K/V tiles arrive
 // by direct global->LDS loads; operands are read one step ahead.
 template <int D, int NW, int BC, int MASK>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int BR = NW * 32;
   constexpr int KC = D / 16;
   constexpr int DT = D / 32;
@@ -808,10 +808,23 @@ __global__ __launch_bounds__(F32B_T) void bwd_dq_f32_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
+// dK/dV (KNW waves of 32 keys) and dQ (QNW waves of 32 queries) launches.
+template <int D, int MASK, int KNW, int QNW>
+static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
+  const int n_kt = (a.N + KNW * 32 - 1) / (KNW * 32);
+  hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<D, KNW, 32, MASK>), dim3((unsigned)(n_kt * a.BH)),
+                     dim3(KNW * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qt = (a.N + QNW * 32 - 1) / (QNW * 32);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, QNW, 64, MASK>), dim3((unsigned)(n_qt * a.BH)),
+                     dim3(QNW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int MASK>
 static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, int cfg, hipStream_t stream) {
   constexpr int KV_NW = 4, KV_BRQ = 64;   // first form: 128 keys per dK/dV workgroup
-  constexpr int KV2_NW = 8, KV2_BRQ = 32; // second form: 256 keys per dK/dV workgroup
   constexpr int Q_NW = 8, Q_BC = 64;      // 256 query rows per dQ workgroup
   const long rows = (long)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
@@ -823,17 +836,19 @@ static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, int cfg, hipStream_t st
     const int n_kt = (a.N + KV_NW * 32 - 1) / (KV_NW * 32);
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, KV_NW, KV_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
                        dim3(KV_NW * 64), 0, stream, a);
-  } else {
-    const int n_kt = (a.N + KV2_NW * 32 - 1) / (KV2_NW * 32);
-    hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<D, KV2_NW, KV2_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
-                       dim3(KV2_NW * 64), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_qt = (a.N + Q_NW * 32 - 1) / (Q_NW * 32);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, Q_NW, Q_BC, MASK>), dim3((unsigned)(n_qt * a.BH)),
+                       dim3(Q_NW * 64), 0, stream, a);
+    return hipGetLastError();
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qt = (a.N + Q_NW * 32 - 1) / (Q_NW * 32);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, Q_NW, Q_BC, MASK>), dim3((unsigned)(n_qt * a.BH)),
-                     dim3(Q_NW * 64), 0, stream, a);
-  return hipGetLastError();
+  // Under a band mask a wave needs only the query (key) rows within the
+  // window of its own 32 keys (queries), while a workgroup streams the union
+  // over its waves: four waves per workgroup keep more of each streamed tile
+  // useful than eight. cfg 2 swaps the choice (timing comparisons).
+  if ((MASK == MASK_LOCAL) != (cfg == 2)) return launch_bwd_main<D, MASK, 4, 4>(a, stream);
+  return launch_bwd_main<D, MASK, 8, 8>(a, stream);
 }
 
 template <int DP, int MASK>

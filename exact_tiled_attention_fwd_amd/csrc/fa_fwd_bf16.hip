@@ -108,7 +108,7 @@ __device__ __forceinline__ float sum16(const f32x16& v) {
 __device__ __forceinline__ constexpr int acc_key(int r) { return 8 * (r >> 2) + (r & 3); }
 
 template <int D, int QB, int NW, int BC, int MASK>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QW = QB * 32;       // query rows per wave
   constexpr int BR = NW * QW;       // query rows per workgroup
@@ -691,20 +691,28 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
 // Kernel choice per head dimension, picked by interleaved timing on MI355X
 // (causal 8192 x 128, 4096 x 128, unmasked 2048 x 64, band 16384 x 128):
 // d = 128 uses the tile kernel with 128-key tiles, d = 64 the block-pipelined
-// kernel with 64-key tiles. cfg selects the alternatives for timing sweeps.
+// kernel with 64-key tiles. Under a band mask a wave needs only the key tiles
+// within the window of its 32 rows while the workgroup streams the union over
+// its waves, so d = 128 bands use four-wave workgroups with 64-key tiles
+// (two per CU): 218 -> 174 us on [1, 32, 16384, 128] with radius 128.
+// cfg selects the alternatives for timing sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
     switch (cfg) {
       case 1: return launch_fwd_bf16_cfg<128, 1, 8, 64>(a, mask, stream);
       case 2: return launch_fwd_bf16_xb<128, 128>(a, mask, stream);
       case 3: return launch_fwd_bf16_xb<128, 64>(a, mask, stream);
-      default: return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
+      case 4: return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
+      default:
+        if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
+        return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
     }
   }
   switch (cfg) {
     case 1: return launch_fwd_bf16_cfg<64, 1, 8, 64>(a, mask, stream);
     case 2: return launch_fwd_bf16_xb<64, 128>(a, mask, stream);
     case 3: return launch_fwd_bf16_cfg<64, 1, 8, 128>(a, mask, stream);
+    case 4: return launch_fwd_bf16_cfg<64, 1, 4, 64>(a, mask, stream);
     default: return launch_fwd_bf16_xb<64, 64>(a, mask, stream);
   }
 }

@@ -55,6 +55,9 @@ WORKLOADS = {
                  seed=4, qk_mult=8.0),
         Workload("bf16_causal_bwd_b2h16_n4096_d128", 2, 16, 4096, 128, "bf16", "causal", seed=5,
                  backward=True),
+        # the band workload's shape and logit scale, for the backward
+        Workload("bf16_local128_x8_bwd_b1h32_n16384_d128", 1, 32, 16384, 128, "bf16", "local",
+                 128, seed=6, qk_mult=8.0, backward=True),
     ]
 }
 

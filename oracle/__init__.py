@@ -50,6 +50,10 @@ def _bind(lib):
     lib.oracle_attn_bwd_dense.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
                                           ctypes.c_double, ctypes.c_int, _i64, _dp, _dp, _dp]
     lib.oracle_attn_bwd_dense.restype = ctypes.c_int
+    lib.oracle_attn_bwd_rows.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_double,
+                                         ctypes.c_int, _i64, _i64p, _i64p, _i64, _i64p, _i64p,
+                                         _i64, _dp, _dp, _dp]
+    lib.oracle_attn_bwd_rows.restype = ctypes.c_int
     return lib
 
 
@@ -182,6 +186,35 @@ class Oracle:
         return {"dq": dq.reshape(sh), "dk": dk.reshape(sh), "dv": dv.reshape(sh),
                 "o": o.reshape(sh), "lse": lse.reshape(lead + (N,)), "D": D.reshape(lead + (N,))}
 
+    def bwd_rows(self, q, k, v, dout, scale, q_bh, q_row, k_bh, k_row, mask="none", window=0):
+        """Backward for chosen rows: dQ of the query rows (q_bh[r], q_row[r])
+        and dK, dV of the key rows (k_bh[r], k_row[r]); heads index the
+        flattened [B*H] axis. Returns dict with dq [nq, d], dk, dv [nk, d]."""
+        q3, _ = _as3(q)
+        k3, _ = _as3(k)
+        v3, _ = _as3(v)
+        do3, _ = _as3(dout)
+        BH, N, d = q3.shape
+        qb = np.ascontiguousarray(q_bh, dtype=np.int64)
+        qr = np.ascontiguousarray(q_row, dtype=np.int64)
+        kb = np.ascontiguousarray(k_bh, dtype=np.int64)
+        kr = np.ascontiguousarray(k_row, dtype=np.int64)
+        for b_, r_ in ((qb, qr), (kb, kr)):
+            if b_.shape != r_.shape or (b_.size and (b_.min() < 0 or b_.max() >= BH or
+                                                     r_.min() < 0 or r_.max() >= N)):
+                raise ValueError("row indices out of range")
+        dq = np.empty((qb.size, d))
+        dk = np.empty((kb.size, d))
+        dv = np.empty((kb.size, d))
+        ip = lambda a: a.ctypes.data_as(_i64p)
+        rc = self.lib.oracle_attn_bwd_rows(_ptr(q3), _ptr(k3), _ptr(v3), _ptr(do3), BH, N, d,
+                                           float(scale), _mask_code(mask), int(window), ip(qb),
+                                           ip(qr), qb.size, ip(kb), ip(kr), kb.size, _ptr(dq),
+                                           _ptr(dk), _ptr(dv))
+        if rc != 0:
+            raise MemoryError("oracle_attn_bwd_rows: allocation failed")
+        return {"dq": dq, "dk": dk, "dv": dv}
+
 
 _default = None
 
@@ -211,3 +244,7 @@ def fwd_tiled(*a, **kw):
 
 def bwd_dense(*a, **kw):
     return default().bwd_dense(*a, **kw)
+
+
+def bwd_rows(*a, **kw):
+    return default().bwd_rows(*a, **kw)

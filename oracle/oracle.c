@@ -286,3 +286,85 @@ int oracle_attn_bwd_dense(const double* q, const double* k, const double* v,
     free(P); free(dS); free(Oh); free(Dh);
     return 0;
 }
+
+/* Backward for chosen rows, by the same chain-rule definition as
+ * oracle_attn_bwd_dense but without N x N matrices, so that sampled
+ * gradients can be checked at full workload sizes:
+ *   dQ of query row (qbh[r], qrow[r]):
+ *     dQ_i = scale sum_j P_ij (<dO_i, v_j> - D_i) k_j  over allowed j;
+ *   dK, dV of key row (kbh[r], krow[r]):
+ *     dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i P_ij (<dO_i, v_j> - D_i) q_i
+ *     over the queries i that may see key j;
+ * with P_ij = exp(z_ij - LSE_i) and D_i = <dO_i, O_i> from the dense row of
+ * query i (dense_row: its own double O and LSE). A key row visits every query
+ * that can see it, each through a dense row: O(N^2 d) per key row without a
+ * band, O(N + window d) per visited query with one. dq_rows is [nq][d],
+ * dk_rows and dv_rows are [nk][d]. Returns 0, or -1 on allocation failure. */
+int oracle_attn_bwd_rows(const double* q, const double* k, const double* v,
+                         const double* dout, int64_t BH, int64_t N, int64_t d, double scale,
+                         int mask, int64_t window, const int64_t* qbh, const int64_t* qrow,
+                         int64_t nq, const int64_t* kbh, const int64_t* krow, int64_t nk,
+                         double* dq_rows, double* dk_rows, double* dv_rows) {
+    (void)BH;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* z = (double*)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double* oi = (double*)malloc((size_t)(d > 0 ? d : 1) * sizeof(double));
+        if (!z || !oi) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nq; ++r) {
+            if (!z || !oi) continue;
+            const size_t off = (size_t)qbh[r] * N * d;
+            const double *Q = q + off, *K = k + off, *V = v + off, *dO = dout + off;
+            const int64_t i = qrow[r];
+            double lse;
+            dense_row(Q, K, V, N, d, scale, mask, window, i, z, oi, &lse);
+            double Di = 0.0;
+            for (int64_t c = 0; c < d; ++c) Di += dO[i * d + c] * oi[c];
+            double* out = dq_rows + r * d;
+            for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                if (z[j] == -INFINITY) continue;
+                double dp = 0.0;
+                for (int64_t c = 0; c < d; ++c) dp += dO[i * d + c] * V[j * d + c];
+                const double ds = exp(z[j] - lse) * (dp - Di);
+                for (int64_t c = 0; c < d; ++c) out[c] += ds * K[j * d + c];
+            }
+            for (int64_t c = 0; c < d; ++c) out[c] *= scale;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nk; ++r) {
+            if (!z || !oi) continue;
+            const size_t off = (size_t)kbh[r] * N * d;
+            const double *Q = q + off, *K = k + off, *V = v + off, *dO = dout + off;
+            const int64_t j = krow[r];
+            double* ok = dk_rows + r * d;
+            double* ov = dv_rows + r * d;
+            for (int64_t c = 0; c < d; ++c) { ok[c] = 0.0; ov[c] = 0.0; }
+            for (int64_t i = 0; i < N; ++i) {
+                if (!oracle_allowed(i, j, mask, window)) continue;
+                double lse;
+                dense_row(Q, K, V, N, d, scale, mask, window, i, z, oi, &lse);
+                double Di = 0.0, dp = 0.0;
+                for (int64_t c = 0; c < d; ++c) {
+                    Di += dO[i * d + c] * oi[c];
+                    dp += dO[i * d + c] * V[j * d + c];
+                }
+                const double p = exp(z[j] - lse);
+                const double ds = p * (dp - Di);
+                for (int64_t c = 0; c < d; ++c) {
+                    ov[c] += p * dO[i * d + c];
+                    ok[c] += ds * Q[i * d + c];
+                }
+            }
+            for (int64_t c = 0; c < d; ++c) ok[c] *= scale;
+        }
+        free(z);
+        free(oi);
+    }
+    return fail ? -1 : 0;
+}

@@ -360,9 +360,26 @@ def pin_backward_against_autograd(orc):
             assert np.max(np.abs(g[name] - t.grad.numpy())) <= 1e-12, (name, mask)
 
 
+def pin_backward_rows_match_dense(orc):
+    """The row-sampled backward (used for full-size sampled checks) returns
+    exactly the rows of the dense backward, which the finite-difference and
+    autograd pins fix, for every mask, edge rows and several heads."""
+    BH, N, d = 3, 29, 5
+    Q, K, V, dO = (_rand((BH, N, d), 120 + t) for t in range(4))
+    qb = np.array([0, 0, 1, 2, 2, 1]); qr = np.array([0, N - 1, 7, 13, 28, 1])
+    kb = np.array([2, 1, 0, 0, 1]); kr = np.array([0, N - 1, 3, 28, 14])
+    for mask, window in (("none", 0), ("causal", 0), ("local", 2), ("local", 0)):
+        ref = orc.bwd_dense(Q, K, V, dO, 0.6, mask, window)
+        got = orc.bwd_rows(Q, K, V, dO, 0.6, qb, qr, kb, kr, mask, window)
+        assert np.max(np.abs(got["dq"] - ref["dq"][qb, qr])) <= 1e-13, mask
+        assert np.max(np.abs(got["dk"] - ref["dk"][kb, kr])) <= 1e-13, mask
+        assert np.max(np.abs(got["dv"] - ref["dv"][kb, kr])) <= 1e-13, mask
+
+
 ALL_PINS = [
     pin_p3_worked_example, pin_p2_recurrence, pin_partial_is_dense_over_prefix,
     pin_tiled_equals_dense_toy, pin_against_library, pin_rows_sum_to_one, pin_large_logits,
     pin_special_cases, pin_mask_matrix, pin_fully_masked_row_in_visited_tile,
     pin_backward_finite_difference, pin_backward_invariants, pin_backward_against_autograd,
+    pin_backward_rows_match_dense,
 ]

@@ -129,3 +129,36 @@ def test_full_size_backward_workload():
     sv = (dvf.sum(dim=2) - dof.sum(dim=2)).norm() / dof.sum(dim=2).norm()
     print(f"invariants: |sum dK|/|dK| = {float(sk):.2e}, |sum dV - sum dO| rel = {float(sv):.2e}")
     assert float(sk) <= 2e-2 and float(sv) <= 1e-2
+
+
+def test_full_size_band_backward():
+    """The band workload's shape and logit scale ([1, 32, 16384, 128], Q and
+    K x8, |i - j| <= 128) through the backward in the default launch
+    configuration: sampled dQ rows and dK/dV rows (edges, tile boundaries and
+    random rows of four heads) against the oracle's row-sampled backward,
+    relative Frobenius error over the sampled rows; plus the invariants on
+    every slice."""
+    w = WORKLOADS["bf16_local128_x8_bwd_b1h32_n16384_d128"]
+    inp = make_inputs(w)
+    q, k, v, do = (G.to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
+    print("full-size band backward", flush=True)
+    o, lse = attention_fwd(q, k, v, w.scale, w.mask, w.window)
+    dq, dk, dv = attention_bwd(q, k, v, o, lse, do, w.scale, w.mask, w.window)
+    torch.cuda.synchronize()
+    B, H, N, d = w.shape
+    bh, rows, heads = G.sample_rows(B * H, N, 40, seed=61)
+    sel = {h_: i for i, h_ in enumerate(heads)}
+    pick = {n: inp[n].reshape(B * H, N, d)[heads] for n in ("q", "k", "v", "dout")}
+    lb = np.array([sel[h_] for h_ in bh])
+    ref = oracle.bwd_rows(pick["q"], pick["k"], pick["v"], pick["dout"], w.scale, lb, rows, lb,
+                          rows, w.mask, w.window)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        gs = G.f64(g.reshape(B * H, N, d)[torch.as_tensor(bh), torch.as_tensor(rows)])
+        e = float(np.linalg.norm(gs - ref[name]) / np.linalg.norm(ref[name]))
+        print(f"{name}: rel {e:.3e} over {len(rows)} rows", flush=True)
+        assert np.all(np.isfinite(gs)) and e <= G.TOL_GRAD_REL, (name, e)
+    dkf, dvf, dof = dk.double(), dv.double(), do.double()
+    sk = dkf.sum(dim=2).norm() / dkf.norm()
+    sv = (dvf.sum(dim=2) - dof.sum(dim=2)).norm() / dof.sum(dim=2).norm()
+    print(f"invariants: |sum dK|/|dK| = {float(sk):.2e}, |sum dV - sum dO| rel = {float(sv):.2e}")
+    assert float(sk) <= 2e-2 and float(sv) <= 1e-2
