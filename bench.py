@@ -19,6 +19,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --std-sweep [--std-n N] [--no-settle]
                                       (fused fa_fwd vs standard fa_fwd_standard, N = 1k..16k)
        python bench.py --summarize-std DIR   (their HBM bytes from per-N counter passes, no GPU)
+       python bench.py --km-sweep [--km-n N] [--km-bc BC] [--no-settle]
+                                      (key-major fa_fwd_keymajor over its key-block sizes)
+       python bench.py --summarize-km DIR    (its HBM bytes vs block size, no GPU)
 """
 import argparse
 import csv
@@ -201,6 +204,13 @@ def main():
                          "(counter passes: only the flushed launches run)")
     ap.add_argument("--summarize-std", default=None,
                     help="HBM bytes of fused vs standard from the per-N counter CSVs in DIR")
+    ap.add_argument("--km-sweep", action="store_true",
+                    help="key-major fa_fwd_keymajor vs the query-major fa_fwd, bf16 [1,16,N,64], "
+                         "no mask, N in {2048, 4096}, key blocks 32..256")
+    ap.add_argument("--km-n", type=int, default=0, help="only this N in --km-sweep")
+    ap.add_argument("--km-bc", type=int, default=0, help="only this key-block size in --km-sweep")
+    ap.add_argument("--summarize-km", default=None,
+                    help="HBM bytes of the key-major forward per block size from counter CSVs in DIR")
     ap.add_argument("--sweep", action="store_true",
                     help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
@@ -210,6 +220,9 @@ def main():
         return
     if args.summarize_std:
         print(summarize_std(args.summarize_std, args.copy_mib))
+        return
+    if args.summarize_km:
+        print(summarize_km(args.summarize_km, args.copy_mib))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
@@ -237,6 +250,9 @@ def main():
         return
     if args.std_sweep:
         std_sweep(torch, fa, dev, args)
+        return
+    if args.km_sweep:
+        km_sweep(torch, fa, dev, args)
         return
 
     have_bwd = not args.fwd_only
@@ -462,6 +478,38 @@ def sweep(torch, fa, dev, args):
                 del q, k, v, do, o, lse, dq, dk, dv, ws
 
 
+def time_unit(torch, fn, stream, scratch, reps, settle=True):
+    """(flushed, warm) milliseconds of fn: 'flushed' is the median of `reps`
+    launches each preceded by a write of `scratch` (evicting L2 and the
+    MALL), event-timed around the launch only; 'warm' the mean of `reps`
+    launches back to back after 0.1 s of them (clock settle), NaN when
+    settle is False (counter passes run only the flushed launches)."""
+    warm = float("nan")
+    if settle:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:
+            fn()
+            torch.cuda.synchronize()
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        for _ in range(reps):
+            fn()
+        e_.record(stream)
+        e_.synchronize()
+        warm = s_.elapsed_time(e_) / reps
+    fl = []
+    for i in range(reps):
+        scratch.fill_(i & 255)
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        fn()
+        e_.record(stream)
+        e_.synchronize()
+        fl.append(s_.elapsed_time(e_))
+    return statistics.median(fl), warm
+
+
 STD_NS = (1024, 2048, 4096, 8192, 16384)
 
 
@@ -497,32 +545,7 @@ def std_sweep(torch, fa, dev, args):
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         units = (lambda: fa.fa_fwd(q, k, v, o, lse, 0.125, "none", 0, stream),
                  lambda: fa.fa_fwd_standard(q, k, v, o, lse, ws, 0.125, "none", 0, stream))
-        res = []
-        for fn in units:
-            warm = float("nan")
-            if not args.no_settle:
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                while time.perf_counter() - t0 < 0.1:
-                    fn()
-                    torch.cuda.synchronize()
-                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s_.record(stream)
-                for _ in range(reps):
-                    fn()
-                e_.record(stream)
-                e_.synchronize()
-                warm = s_.elapsed_time(e_) / reps
-            fl = []
-            for i in range(reps):
-                scratch.fill_(i & 255)
-                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s_.record(stream)
-                fn()
-                e_.record(stream)
-                e_.synchronize()
-                fl.append(s_.elapsed_time(e_))
-            res.append((statistics.median(fl), warm))
+        res = [time_unit(torch, fn, stream, scratch, reps, not args.no_settle) for fn in units]
         fb, sb = std_bytes(N, B, H, d)
         (ff, fw), (sf, sw) = res
         print(f"| {N} | {ff * 1e3:.1f} | {fw * 1e3:.1f} | {sf * 1e3:.1f} | {sw * 1e3:.1f} | "
@@ -566,6 +589,110 @@ def summarize_std(d, copy_mib):
         fm, sm = sum(sums["fused"]), sum(sums["standard"])
         lines.append(f"| {N} | {fm / 1e6:.1f} ({fb / 1e6:.1f}) | {sm / 1e6:.1f} ({sb / 1e6:.1f}) | "
                      f"{sm / fm:.1f} |")
+    lines += ["", f"Calibration: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f} "
+              f"(a {copy_mib} MiB copy through `{ck}`)."]
+    return "\n".join(lines)
+
+
+KM_NS = (2048, 4096)
+KM_BCS = (32, 64, 128, 256)
+
+
+def km_bytes(N, bc, B=1, H=16, d=64):
+    """Model of the key-major forward's device-memory bytes at bf16 [B,H,N,d]:
+    each of the T_c = ceil(N/bc) launches reads all of Q and reads and writes
+    the running state of every row (two lanes x (d/2 + 2) floats); K and V
+    are read once per head and launch (L2 serves the other workgroups); the
+    finalize pass reads the state once more and writes O and LSE."""
+    tc = -(-N // bc)
+    rows = B * H * (-(-N // 256)) * 256
+    state = rows * 2 * (d // 2 + 2) * 4
+    per_launch = B * H * N * d * 2 + 2 * state + B * H * bc * d * 2 * 2
+    return state + tc * per_launch + state + B * H * N * (d * 2 + 4)
+
+
+def km_sweep(torch, fa, dev, args):
+    """The key-major forward (outer loop over key blocks, state through
+    device memory) against the query-major fa_fwd on bf16 [1, 16, N, 64]
+    without a mask: time and modelled bytes per key-block size."""
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(args.steps, 3)
+    print("| N | order | key block B_c | launches | flushed µs | warm µs | modelled bytes (MB) |")
+    print("|---|---|---|---|---|---|---|")
+    B, H, d = 1, 16, 64
+    for N in ([args.km_n] if args.km_n else KM_NS):
+        g = torch.Generator(device=dev).manual_seed(130363 + N)
+        q, k, v = (torch.randn(B, H, N, d, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_fwd_keymajor_workspace_bytes(B, H, N, d, q.dtype), dtype=torch.uint8,
+                         device=dev)
+        if not args.km_bc:
+            f, w = time_unit(torch, lambda: fa.fa_fwd(q, k, v, o, lse, 0.125, "none", 0, stream),
+                             stream, scratch, reps, not args.no_settle)
+            fb, _ = std_bytes(N, B, H, d)
+            print(f"| {N} | query-major (fa_fwd) | — | 1 | {f * 1e3:.1f} | {w * 1e3:.1f} | "
+                  f"{fb / 1e6:.1f} |", flush=True)
+        for bc in ([args.km_bc] if args.km_bc else KM_BCS):
+            f, w = time_unit(torch, lambda: fa.fa_fwd_keymajor(q, k, v, o, lse, ws, 0.125, "none",
+                                                               0, bc, stream),
+                             stream, scratch, reps, not args.no_settle)
+            print(f"| {N} | key-major | {bc} | {-(-N // bc) + 2} | {f * 1e3:.1f} | {w * 1e3:.1f} | "
+                  f"{km_bytes(N, bc, B, H, d) / 1e6:.1f} |", flush=True)
+        del q, k, v, o, lse, ws
+
+
+def summarize_km(d, copy_mib):
+    """Measured device-memory bytes of one key-major forward per (N, B_c)
+    from counter CSVs fetch_N<n>_bc<b>_*, write_N<n>_bc<b>_* (summed over
+    the init, step and finalize launches of one call), against km_bytes()."""
+    one = lambda pat: sorted(glob.glob(os.path.join(d, pat)))[0]
+    cf = _pmc_per_dispatch(one("copy_fetch*_counter_collection.csv"), "FETCH_SIZE")
+    cw = _pmc_per_dispatch(one("copy_write*_counter_collection.csv"), "WRITE_SIZE")
+    ck = [n for n in cf if "copy" in n.lower()][0]
+    nbytes = copy_mib * (1 << 20)
+    f_fetch, f_write = nbytes / (cf[ck] * 1024.0), nbytes / (cw[ck] * 1024.0)
+
+    def per_call(path, counter):
+        """Per call: sum over one call's dispatches of the km_* kernels
+        (calls are identical, so total / number of finalize launches)."""
+        tot, calls = 0.0, 0
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter or "km_" not in r["Kernel_Name"]:
+                    continue
+                tot += float(r["Counter_Value"])
+                calls += "finalize" in r["Kernel_Name"]
+        return tot / max(calls, 1)
+
+    lines = ["| N | B_c | measured read MB | measured written MB | measured total MB | modelled MB |",
+             "|---|---|---|---|---|---|"]
+    pts = []
+    for N in KM_NS:
+        for bc in KM_BCS:
+            fp = glob.glob(os.path.join(d, f"fetch_N{N}_bc{bc}_counter_collection.csv"))
+            wp = glob.glob(os.path.join(d, f"write_N{N}_bc{bc}_counter_collection.csv"))
+            if not fp or not wp:
+                continue
+            rb = per_call(fp[0], "FETCH_SIZE") * 1024.0 * f_fetch
+            wb = per_call(wp[0], "WRITE_SIZE") * 1024.0 * f_write
+            pts.append((N, bc, rb + wb))
+            lines.append(f"| {N} | {bc} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} | "
+                         f"{km_bytes(N, bc) / 1e6:.1f} |")
+    # bytes ~ a + b * N^2 / B_c at fixed d: least squares over the points
+    if len(pts) >= 3:
+        xs = [N * N / bc for N, bc, _ in pts]
+        ys = [y for _, _, y in pts]
+        n = len(xs)
+        mx, my = sum(xs) / n, sum(ys) / n
+        b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+        a = my - b * mx
+        ss = sum((y - my) ** 2 for y in ys)
+        r2 = 1 - sum((y - (a + b * x)) ** 2 for x, y in zip(xs, ys)) / ss if ss > 0 else 1.0
+        lines += ["", f"Least-squares fit bytes = a + b * N^2 / B_c: a = {a / 1e6:.1f} MB, "
+                  f"b = {b:.1f} bytes, R^2 = {r2:.4f}."]
     lines += ["", f"Calibration: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f} "
               f"(a {copy_mib} MiB copy through `{ck}`)."]
     return "\n".join(lines)

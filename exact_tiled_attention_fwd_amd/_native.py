@@ -54,6 +54,11 @@ def load():
     lib.fa_fwd_standard.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                     i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_standard.restype = i
+    lib.fa_fwd_keymajor_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_keymajor_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_keymajor.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                    i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_keymajor.restype = i
     dp = ctypes.POINTER(ctypes.c_double)
     lib.fa_probe_mfma_bf16.argtypes = [i, vp, dp]
     lib.fa_probe_mfma_bf16.restype = i
@@ -149,6 +154,33 @@ def fa_fwd_standard(q, k, v, o, lse, workspace, scale, mask=None, window=0, stre
                                 _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_fwd_standard")
+
+
+def fa_fwd_keymajor_workspace_bytes(B, H, N, d, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().fa_fwd_keymajor_workspace_bytes(int(B), int(H), int(N), int(d), code))
+
+
+def fa_fwd_keymajor(q, k, v, o, lse, workspace, scale, mask=None, window=0, block_keys=64,
+                    stream=None):
+    """Call fa_fwd_keymajor (outer loop over key blocks of `block_keys`, the
+    running state in `workspace`, a uint8 GPU tensor of at least
+    fa_fwd_keymajor_workspace_bytes(...) bytes) on bf16 [B, H, N, d] tensors."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check("q", q)
+    for n, t in (("k", k), ("v", v), ("o", o)):
+        _check(n, t, q, q.dtype, q.shape)
+    _check("lse", lse, q, torch.float32, (B, H, N))
+    _check("workspace", workspace, q)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = load().fa_fwd_keymajor(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), workspace.data_ptr(), wbytes, B, H, N, d,
+                                _dtype_code(q), float(scale), _mask_code(mask), int(window),
+                                int(block_keys), _stream(q, stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd_keymajor")
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -190,4 +190,55 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+size_t fa_fwd_keymajor_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
+  if (dtype != FA_BF16) return 0;
+  if (check_problem(B, H, N, d, dtype, 1.0f, FA_MASK_NONE, 0) != FA_OK) return 0;
+  return fa::km_state_bytes(B * H, N, d);
+}
+
+fa_status fa_fwd_keymajor(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                          fa_dtype dtype, float scale, fa_mask mask, int window, int block_keys,
+                          void* stream) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  const bool bc_ok = block_keys == 32 || block_keys == 64 || block_keys == 128 ||
+                     (block_keys == 256 && d == 64);
+  if (!bc_ok) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  const size_t total = fa::km_state_bytes(B * H, N, d);
+  if (!workspace || workspace_bytes < total) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins)
+    if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb) || overlap(workspace, total, in, tb))
+      return FA_ERR_ALIAS;
+  if (overlap(o, tb, lse, lb) || overlap(workspace, total, o, tb) || overlap(workspace, total, lse, lb))
+    return FA_ERR_ALIAS;
+  fa::FwdArgs f;
+  bf16_scale(scale, f);
+  fa::KmArgs a;
+  a.q = (const bf16*)q;
+  a.k = (const bf16*)k;
+  a.v = (const bf16*)v;
+  a.o = (bf16*)o;
+  a.lse = lse;
+  a.state = (float*)workspace;
+  a.BH = B * H;
+  a.N = N;
+  a.n_qtiles = 0;
+  a.window = mask == FA_MASK_LOCAL ? window : 0;
+  a.scale_log2 = f.scale_log2;
+  a.scale_abs = f.scale_abs;
+  a.q_and = f.q_and;
+  a.q_xor = f.q_xor;
+  const hipError_t e = fa::launch_fwd_keymajor(a, d, block_keys, (int)mask, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"

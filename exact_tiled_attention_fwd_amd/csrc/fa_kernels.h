@@ -51,6 +51,26 @@ struct StdArgs {
   float scale;  // signed scale as given
 };
 
+// Key-major forward: per key block one launch updating a running state.
+struct KmArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  float* state;       // workspace: km_state_bytes(BH, N, d)
+  int BH;
+  int N;
+  int n_qtiles;       // filled by the launcher
+  int window;
+  float scale_log2;   // as FwdArgs
+  float scale_abs;
+  unsigned q_and;
+  unsigned q_xor;
+};
+size_t km_state_bytes(int BH, int N, int d);
+hipError_t launch_fwd_keymajor(const KmArgs& a, int d, int bc, int mask, hipStream_t stream);
+
 // cfg selects a tile configuration (0 = default); tuning only.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream);
 hipError_t launch_std_bf16(const StdArgs& a, int d, int mask, hipStream_t stream);

@@ -11,19 +11,9 @@
 // ldp = N rounded up to 8 (16-byte aligned rows).
 #include "fa_common.h"
 #include "fa_kernels.h"
+#include "fa_tile_ops.h"
 
 namespace fa {
-
-template <int D>
-__device__ __forceinline__ int swz_std(int row) {  // 16-byte chunk swizzle of K/V rows
-  if constexpr (D == 128) return row & 15;
-  else return (row >> 1) & 7;
-}
-template <int D>
-__device__ __forceinline__ int swz_std_v(int row) {  // V rows read transposed
-  if constexpr (D == 128) return (row & 3) << 2;
-  else return ((row >> 1) & 1) << 2;
-}
 
 // ---- step 1: S = scale Q K^T. Workgroup: 256 queries (8 waves x 32) x 128
 // keys. S = Q K^T with Q as the A operand puts the key on the lane, so each
@@ -52,7 +42,7 @@ __global__ __launch_bounds__(512) void std_scores_kernel(StdArgs a) {
     const int row = p / CPR;
     int gr = k0 + row;
     gr = gr < N ? gr : N - 1;
-    lds_dma16(a.k + base + (size_t)gr * D + ((p % CPR) ^ swz_std<D>(row)) * 8, lds_addr(sK + slot * 16));
+    lds_dma16(a.k + base + (size_t)gr * D + ((p % CPR) ^ swz_k16<D>(row)) * 8, lds_addr(sK + slot * 16));
   }
   bf16x8 qop[KC];
   const int qi = q0 + l32;
@@ -75,7 +65,7 @@ __global__ __launch_bounds__(512) void std_scores_kernel(StdArgs a) {
     const int row = kb * 32 + l32;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const bf16x8 kop = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_std<D>(row)) << 4));
+      const bf16x8 kop = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[kc], kop, acc, 0, 0, 0);
     }
     const int key = k0 + kb * 32 + l32;
@@ -165,7 +155,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
       const int row = p / CPR;
       int gr = t * BC + row;
       gr = gr < N ? gr : N - 1;  // P is 0 for keys past N
-      lds_dma16(a.v + base + (size_t)gr * D + ((p % CPR) ^ swz_std_v<D>(row)) * 8,
+      lds_dma16(a.v + base + (size_t)gr * D + ((p % CPR) ^ swz_v16<D>(row)) * 8,
                 lds_addr(sV + buf * TILEB + slot * 16));
     }
   };
@@ -199,8 +189,8 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
-          const int clo = ((dt * 8 + tr_ch8) ^ (swz_std_v<D>(rlo) << 1)) * 8;
-          const int chi = ((dt * 8 + tr_ch8) ^ (swz_std_v<D>(rhi) << 1)) * 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
           const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sVb + rlo * ROWB + clo));
           const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sVb + rhi * ROWB + chi));
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));

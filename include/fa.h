@@ -133,6 +133,39 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
                           int B, int H, int N, int d, fa_dtype dtype,
                           float scale, fa_mask mask, int window, void* stream);
 
+/*
+ * Bytes of device workspace fa_fwd_keymajor needs: the running state of
+ * every query row (float32 unnormalized output, maximum and denominator,
+ * held by two lanes per row), B*H*ceil(N/256)*512*(d/2 + 2)*4 bytes.
+ * Returns 0 for an invalid problem or
+ * a dtype other than FA_BF16.
+ */
+size_t fa_fwd_keymajor_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Key-major forward, the loop order of the FlashAttention paper's
+ * Algorithm 1 as quoted in "What the tiling is actually constrained by"
+ * (section "The formula, which the title only gestures at": K and V split
+ * into T_c = ceil(N / B_c) blocks of B_c keys, block_keys here) and named in
+ * the TensorViz card's fidelity note. The outer loop runs over key blocks
+ * (one launch each); every launch updates the running state of all query
+ * rows with the rule of the Hinglish notes' "Derivation: Incremental
+ * Softmax" (Steps 2-3), reading the state from `workspace` and writing it
+ * back, so its device-memory traffic grows as N^2 d / B_c. Same O and LSE
+ * contract as fa_fwd (bf16 only), for comparison with fa_fwd's query-major
+ * order.
+ *   block_keys : 32, 64 or 128; also 256 when d == 64.
+ *   workspace  : at least fa_fwd_keymajor_workspace_bytes(...) bytes, owned
+ *                by the caller, 16-byte aligned, not overlapping any tensor;
+ *                contents ignored on entry and undefined on return.
+ * Errors: as fa_fwd; FA_ERR_DTYPE for FA_F32; FA_ERR_SHAPE for an
+ * unsupported block_keys; FA_ERR_WORKSPACE.
+ */
+fa_status fa_fwd_keymajor(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int H, int N, int d, fa_dtype dtype,
+                          float scale, fa_mask mask, int window, int block_keys, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);
 

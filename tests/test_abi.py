@@ -115,3 +115,19 @@ def test_standard_workspace_and_errors(lib):
     assert call(ws=None) == 8 and call(wb=16) == 8
     assert call(ws=ctypes.c_void_p(0x4000008)) == 7
     assert call(ws=ctypes.c_void_p(0x100000)) == 10   # workspace overlaps q
+
+
+def test_keymajor_workspace_and_errors(lib):
+    # two lanes per query row, 256-row workgroups: 512 * (d/2 + 2) floats each
+    assert lib.fa_fwd_keymajor_workspace_bytes(2, 3, 300, 128, 1) == 2 * 3 * 2 * 512 * 66 * 4
+    assert lib.fa_fwd_keymajor_workspace_bytes(1, 1, 256, 64, 1) == 512 * 34 * 4
+    assert lib.fa_fwd_keymajor_workspace_bytes(1, 1, 256, 64, 0) == 0
+    ws = ctypes.c_void_p(0x4000000)
+    def call(bc=64, d=64, dtype=1, ws=ws, wb=1 << 30):
+        return lib.fa_fwd_keymajor(FAKE, FAKE, FAKE, ctypes.c_void_p(0x200000),
+                                   ctypes.c_void_p(0x900000), ws, wb, 1, 1, 8, d, dtype, 0.125,
+                                   0, 0, bc, None)
+    assert call(bc=48) == 2 and call(bc=256, d=128) == 2 and call(bc=512) == 2
+    assert call(dtype=0) == 3
+    assert call(ws=None) == 8 and call(wb=100) == 8
+    assert call(ws=ctypes.c_void_p(0x4000004)) == 7
