@@ -11,8 +11,8 @@
 //
 // Three launches on the caller's stream, no atomics, deterministic:
 //  1. preprocess: D_i for every row (reads O and dO once).
-//  2. dK/dV, key-major: a workgroup owns a block of keys (K, V kept in
-//     registers as MFMA B operands) and streams every query tile that sees
+//  2. dK/dV, key-major: a workgroup owns a block of keys (K in registers and
+//     V in LDS as MFMA B operands) and streams every query tile that sees
 //     them through LDS. S = Q K^T puts the key on the lane, so P^T and dS^T
 //     are already the A operands of dV += P^T dO and dK += dS^T Q; the B
 //     operands (dO, Q with the query along the lane vector) come from
@@ -64,215 +64,12 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const bf16* __restric
 }
 
 // ------------------------------------------------------------------ dK / dV
-template <int D, int NW, int BRQ, int MASK>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BC = NW * 32;     // keys per workgroup (32 per wave)
-  constexpr int KC = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int QBN = BRQ / 32;   // 32-row query blocks per tile
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = BRQ * ROWB;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BRQ * CPR / NT;
-  static_assert((BRQ * CPR) % NT == 0 && BRQ <= NT, "tile must divide over the threads");
-
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // Q[2], dO[2]
-  __shared__ __attribute__((aligned(16))) float sL[2][BRQ];      // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][BRQ];      // D
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int N = a.N;
-  const int n_kt = (N + BC - 1) / BC;
-  int bh, kt;  // ascending: under a causal mask the first key tiles see most rows
-  wg_tile(blockIdx.x, a.BH, n_kt, bh, kt);
-  const size_t base = (size_t)bh * N * D;
-  const bf16* __restrict__ Q = (const bf16*)a.q + base;
-  const bf16* __restrict__ K = (const bf16*)a.k + base;
-  const bf16* __restrict__ V = (const bf16*)a.v + base;
-  const bf16* __restrict__ dO = (const bf16*)a.dout + base;
-  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
-  const float* __restrict__ Dl = a.delta + (size_t)bh * N;
-  const int k0 = kt * BC;
-  const int kw0 = k0 + wv * 32;
-  const int key = kw0 + l32;  // this lane's key in the S / dP accumulators
-
-  bf16x8 kop[KC], vop[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < N) {
-      x = *(const u32x4*)(K + (size_t)key * D + kc * 16 + h * 8);
-      y = *(const u32x4*)(V + (size_t)key * D + kc * 16 + h * 8);
-    }
-    x = (x & a.q_and) ^ a.q_xor;  // sign / zero of the scale folded into K
-    kop[kc] = __builtin_bit_cast(bf16x8, x);
-    vop[kc] = __builtin_bit_cast(bf16x8, y);
-  }
-  f32x16 dk[DT], dv[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[dt][r] = 0.f;
-      dv[dt][r] = 0.f;
-    }
-  const float c = a.scale_log2;
-  const float LOG2E = 1.4426950408889634f;
-
-  // query rows that can see keys [k0, k0 + BC)
-  int q_lo = 0, q_hi = N;
-  if (MASK == MASK_CAUSAL) q_lo = k0;
-  if (MASK == MASK_LOCAL) {
-    q_lo = k0 - a.window > 0 ? k0 - a.window : 0;
-    const long long hh = (long long)k0 + BC + a.window;
-    q_hi = hh < N ? (int)hh : N;
-  }
-  const int t_begin = q_lo / BRQ, t_end = q_lo < q_hi ? (q_hi + BRQ - 1) / BRQ : t_begin;
-
-  u32x4 stQ[CPT], stO[CPT];
-  float stL = 0.f, stD = 0.f;
-  auto gload = [&](int t) {
-    const int r0 = t * BRQ;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int gr = r0 + row;
-      u32x4 zq = {0u, 0u, 0u, 0u}, zo = {0u, 0u, 0u, 0u};
-      if (gr < N) {
-        zq = *(const u32x4*)(Q + (size_t)gr * D + cc * 8);
-        zo = *(const u32x4*)(dO + (size_t)gr * D + cc * 8);
-      }
-      stQ[i] = zq;
-      stO[i] = zo;
-    }
-    if (tid < BRQ) {
-      const int gr = r0 + tid;
-      stL = gr < N ? LSE[gr] * LOG2E : INFINITY;  // padded rows get P = 0
-      stD = gr < N ? Dl[gr] : 0.f;
-    }
-  };
-  auto lstore = [&](int buf) {
-    char* sQ = smem + buf * TILEB;
-    char* sO = smem + (2 + buf) * TILEB;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int off = row * ROWB + ((cc ^ swz_dual<D>(row)) << 4);
-      *(u32x4*)(sQ + off) = stQ[i];
-      *(u32x4*)(sO + off) = stO[i];
-    }
-    if (tid < BRQ) {
-      sL[buf][tid] = stL;
-      sD[buf][tid] = stD;
-    }
-  };
-
-  if (t_begin < t_end) {
-    gload(t_begin);
-    lstore(0);
-  }
-  __syncthreads();
-
-  const int g16 = lane >> 4, s16 = lane & 15;
-  const int tr_row = 4 * h + (s16 >> 2);
-  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const char* sQ = smem + buf * TILEB;
-    const char* sO = smem + (2 + buf) * TILEB;
-    if (t + 1 < t_end) gload(t + 1);
-    const int q0 = t * BRQ;
-#pragma unroll
-    for (int qb = 0; qb < QBN; ++qb) {
-      const int qr0 = q0 + qb * 32;
-      // S = Q K^T and dP = dO V^T: accumulator lane <-> key, 16 query rows
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const int arow = qb * 32 + l32;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int off = arow * ROWB + (((2 * kc + h) ^ swz_dual<D>(arow)) << 4);
-        const bf16x8 qa = *(const bf16x8*)(sQ + off);
-        const bf16x8 oa = *(const bf16x8*)(sO + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[kc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vop[kc], dp, 0, 0, 0);
-      }
-      const bool need_mask = !tile_full<MASK>(qr0, qr0 + 32, kw0, kw0 + 32, a.window);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 L4 = *(const f32x4*)&sL[buf][qb * 32 + 8 * rr + 4 * h];
-        const f32x4 D4 = *(const f32x4*)&sD[buf][qb * 32 + 8 * rr + 4 * h];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rr + e;
-          float sv = s[r];
-          if (need_mask && !allowed<MASK>(qr0 + 8 * rr + 4 * h + e, key, a.window)) sv = -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -L4[e]));
-          s[r] = p;
-          dp[r] = p * (dp[r] - D4[e]);
-        }
-      }
-      // dV += P^T dO and dK += dS^T Q (A operands straight from registers)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pa, da;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pa[e] = (bf16)s[8 * u + e];
-          da[e] = (bf16)dp[8 * u + e];
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          i16x4 olo, ohi, qlo, qhi;
-          const int rlo = qb * 32 + 16 * u + tr_row, rhi = rlo + 8;
-          const int clo = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rlo) << 1)) * 8;
-          const int chi = ((dt * 8 + tr_ch8) ^ (swz_dual<D>(rhi) << 1)) * 8;
-          olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sO + rlo * ROWB + clo));
-          ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sO + rhi * ROWB + chi));
-          qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sQ + rlo * ROWB + clo));
-          qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sQ + rhi * ROWB + chi));
-          const bf16x8 ob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
-          const bf16x8 qbv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ob, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qbv, dk[dt], 0, 0, 0);
-        }
-      }
-    }
-    if (t + 1 < t_end) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // lane holds value column dt*32 + l32 of keys kw0 + 8(r/4) + 4h + (r%4)
-  bf16* __restrict__ dK = (bf16*)a.dk + base;
-  bf16* __restrict__ dV = (bf16*)a.dv + base;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (kr < N) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dK[(size_t)kr * D + dt * 32 + l32] = (bf16)(dk[dt][r] * a.scale);
-        dV[(size_t)kr * D + dt * 32 + l32] = (bf16)dv[dt][r];
-      }
-    }
-  }
-}
-
-// dK/dV, second form: eight waves (two per SIMD) of 32 keys each. To fit
-// two waves per SIMD next to the dK/dV accumulators, the V operand of
+// dK/dV, key-major: NW waves (two per SIMD) of 32 keys each. To fit two
+// waves per SIMD next to the dK/dV accumulators, the V operand of
 // dP = dO V^T is read from an LDS copy of the workgroup's V rows (loaded
-// once) instead of registers; K stays in registers. Q/dO tiles arrive by
-// direct global->LDS loads, and every LDS operand is read one step ahead of
-// the MFMA that consumes it.
+// once) instead of registers; K stays in registers. Q/dO tiles of 32 rows
+// arrive by direct global->LDS loads, and every LDS operand is read one step
+// ahead of the MFMA that consumes it.
 template <int D>
 __device__ __forceinline__ int swz_rows(int row) {  // 16-byte chunk swizzle for row reads
   if constexpr (D == 128) return row & 15;
@@ -824,25 +621,12 @@ static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
 
 template <int D, int MASK>
 static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, int cfg, hipStream_t stream) {
-  constexpr int KV_NW = 4, KV_BRQ = 64;   // first form: 128 keys per dK/dV workgroup
-  constexpr int Q_NW = 8, Q_BC = 64;      // 256 query rows per dQ workgroup
   const long rows = (long)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
                      0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (cfg == 1) {
-    const int n_kt = (a.N + KV_NW * 32 - 1) / (KV_NW * 32);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, KV_NW, KV_BRQ, MASK>), dim3((unsigned)(n_kt * a.BH)),
-                       dim3(KV_NW * 64), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int n_qt = (a.N + Q_NW * 32 - 1) / (Q_NW * 32);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, Q_NW, Q_BC, MASK>), dim3((unsigned)(n_qt * a.BH)),
-                       dim3(Q_NW * 64), 0, stream, a);
-    return hipGetLastError();
-  }
   // Under a band mask a wave needs only the query (key) rows within the
   // window of its own 32 keys (queries), while a workgroup streams the union
   // over its waves: four waves per workgroup keep more of each streamed tile
@@ -871,7 +655,7 @@ static hipError_t launch_bwd_f32_mask(const BwdArgs& a, hipStream_t stream) {
 template <int MASK>
 static hipError_t launch_bwd_mask(const BwdArgs& a, int bf16_path, hipStream_t stream) {
   if (bf16_path) {
-    const char* env = getenv("FA_BWD_CFG");  // tuning only: 1 selects the first dK/dV form
+    const char* env = getenv("FA_BWD_CFG");  // tuning only: 2 swaps the workgroup size choice
     const int cfg = env ? atoi(env) : 0;
     if (a.d == 128) return launch_bwd_bf16_mask<128, MASK>(a, cfg, stream);
     return launch_bwd_bf16_mask<64, MASK>(a, cfg, stream);
