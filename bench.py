@@ -211,6 +211,9 @@ def main():
     ap.add_argument("--km-bc", type=int, default=0, help="only this key-block size in --km-sweep")
     ap.add_argument("--summarize-km", default=None,
                     help="HBM bytes of the key-major forward per block size from counter CSVs in DIR")
+    ap.add_argument("--summarize-util", default=None,
+                    help="summarize unit-utilization counter passes (MfmaUtil, VALUBusy, LdsUtil, "
+                         "...) in DIR per kernel (no GPU)")
     ap.add_argument("--sweep", action="store_true",
                     help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
@@ -223,6 +226,9 @@ def main():
         return
     if args.summarize_km:
         print(summarize_km(args.summarize_km, args.copy_mib))
+        return
+    if args.summarize_util:
+        print(summarize_util(args.summarize_util))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
@@ -695,6 +701,36 @@ def summarize_km(d, copy_mib):
                   f"b = {b:.1f} bytes, R^2 = {r2:.4f}."]
     lines += ["", f"Calibration: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f} "
               f"(a {copy_mib} MiB copy through `{ck}`)."]
+    return "\n".join(lines)
+
+
+def summarize_util(d):
+    """Per attention kernel, the mean over its dispatches of every counter
+    or derived metric found in the counter CSVs of directory d (one column
+    per counter, passes merged)."""
+    vals = {}
+    for path in sorted(glob.glob(os.path.join(d, "*_counter_collection.csv"))):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "")
+                if "fa::" not in name or "probe" in name:
+                    continue
+                key = (name, r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (name, ctr, _), v in per.items():
+            vals.setdefault(name, {}).setdefault(ctr, []).append(v)
+    ctrs = sorted({c for x in vals.values() for c in x})
+    lines = ["| Kernel | dispatches | " + " | ".join(ctrs) + " |",
+             "|---|---|" + "---|" * len(ctrs)]
+    for name in sorted(vals):
+        x = vals[name]
+        n = max(len(v) for v in x.values())
+        cells = []
+        for c in ctrs:
+            v = x.get(c)
+            cells.append("—" if not v else (f"{sum(v) / len(v):.4g}"))
+        lines.append(f"| `{name}` | {n} | " + " | ".join(cells) + " |")
     return "\n".join(lines)
 
 

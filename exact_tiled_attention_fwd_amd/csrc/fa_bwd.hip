@@ -156,18 +156,46 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
   }
   const bool wave_live = kw0 < N;
 
+  // Q/dO tile t -> LDS: per-lane byte offsets within a tile computed once,
+  // the tile's first row as a wave-uniform base; rows past N (last tile
+  // only) read row N-1 (their P is 0)
+  constexpr int IPW = (NINS + NW - 1) / NW;  // DMA instructions per wave
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  unsigned qoff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int p = (wvu + j * NW) * 64 + lane;
+    const int row = p / CPR;
+    qoff[j] = row * ROWB + (((p % CPR) ^ swz_dual<D>(row)) << 4);
+  }
   auto dma = [&](int t, int buf) {
     char* sQ = sQO + buf * QTILEB;
     char* sO = sQO + (2 + buf) * QTILEB;
-    for (int ins = wv; ins < NINS; ins += NW) {
-      const int slot = ins * 64;
-      const int p = slot + lane;
-      const int row = p / CPR;
-      int gr = t * BRQ + row;
-      gr = gr < N ? gr : N - 1;
-      const int cc = (p % CPR) ^ swz_dual<D>(row);
-      lds_dma16(Q + (size_t)gr * D + cc * 8, lds_addr(sQ + slot * 16));
-      lds_dma16(dO + (size_t)gr * D + cc * 8, lds_addr(sO + slot * 16));
+    const int r0 = t * BRQ;
+    const char* gQ = (const char*)Q + (size_t)r0 * ROWB;
+    const char* gO = (const char*)dO + (size_t)r0 * ROWB;
+    if (r0 + BRQ <= N) {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int ins = wvu + j * NW;
+        if (ins < NINS) {
+          lds_dma16_s(gQ, qoff[j], lds_addr(sQ + ins * 64 * 16));
+          lds_dma16_s(gO, qoff[j], lds_addr(sO + ins * 64 * 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int ins = wvu + j * NW;
+        if (ins < NINS) {
+          const int p = ins * 64 + lane;
+          const int row = p / CPR;
+          const unsigned off =
+              min(row, N - 1 - r0) * ROWB + (((p % CPR) ^ swz_dual<D>(row)) << 4);
+          lds_dma16_s(gQ, off, lds_addr(sQ + ins * 64 * 16));
+          lds_dma16_s(gO, off, lds_addr(sO + ins * 64 * 16));
+        }
+      }
     }
   };
   float stL = 0.f, stD = 0.f;
@@ -228,6 +256,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
         va[sl] = *(const bf16x8*)(sVt + vrow * ROWB + (((2 * kc + h) ^ swz_rows<D>(vrow)) << 4));
       };
       rd(0, 0);
+      // the first chunk's reads stand alone, so that every group below pairs
+      // the reads of chunk kc + 1 with the MFMAs of chunk kc
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         if (kc + 1 < KC) rd(kc + 1, (kc + 1) & 1);
@@ -361,18 +392,45 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   key_range<MASK>(qw0, qw0 + 32, N, a.window, wk_lo, wk_hi);
   const bool wave_live = qw0 < N;
 
+  // K/V tile t -> LDS, addressed as in the dK/dV kernel (keys past N, last
+  // tile only, read row N-1 and are masked)
+  constexpr int IPW = (NINS + NW - 1) / NW;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  unsigned koff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int p = (wvu + j * NW) * 64 + lane;
+    const int row = p / CPR;
+    koff[j] = row * ROWB + (((p % CPR) ^ swz_dual<D>(row)) << 4);
+  }
   auto dma = [&](int t, int buf) {
     char* sK = smem + buf * TILEB;
     char* sV = smem + (2 + buf) * TILEB;
-    for (int ins = wv; ins < NINS; ins += NW) {
-      const int slot = ins * 64;
-      const int p = slot + lane;
-      const int row = p / CPR;
-      int gr = t * BC + row;
-      gr = gr < N ? gr : N - 1;  // keys past N are masked
-      const int cc = (p % CPR) ^ swz_dual<D>(row);
-      lds_dma16(K + (size_t)gr * D + cc * 8, lds_addr(sK + slot * 16));
-      lds_dma16(V + (size_t)gr * D + cc * 8, lds_addr(sV + slot * 16));
+    const int k0 = t * BC;
+    const char* gK = (const char*)K + (size_t)k0 * ROWB;
+    const char* gV = (const char*)V + (size_t)k0 * ROWB;
+    if (k0 + BC <= N) {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int ins = wvu + j * NW;
+        if (ins < NINS) {
+          lds_dma16_s(gK, koff[j], lds_addr(sK + ins * 64 * 16));
+          lds_dma16_s(gV, koff[j], lds_addr(sV + ins * 64 * 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int ins = wvu + j * NW;
+        if (ins < NINS) {
+          const int p = ins * 64 + lane;
+          const int row = p / CPR;
+          const unsigned off =
+              min(row, N - 1 - k0) * ROWB + (((p % CPR) ^ swz_dual<D>(row)) << 4);
+          lds_dma16_s(gK, off, lds_addr(sK + ins * 64 * 16));
+          lds_dma16_s(gV, off, lds_addr(sV + ins * 64 * 16));
+        }
+      }
     }
   };
   if (t_begin < t_end) dma(t_begin, 0);
@@ -407,6 +465,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
           va[sl] = *(const bf16x8*)(sV + off);
         };
         rd(0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // as in the dK/dV kernel
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           if (kc + 1 < KC) rd(kc + 1, (kc + 1) & 1);

@@ -33,6 +33,16 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_base) {
                : "memory", "m0");
 }
 
+// The same copy addressed as a wave-uniform 64-bit base (SGPR pair) plus a
+// per-lane 32-bit byte offset: no per-lane 64-bit address arithmetic, and
+// the offsets of a tile can be computed once and reused for every tile.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 // Workgroup id -> (head, tile rank); rank 0 is launched first.
 // Workgroup ids are handed to the eight XCDs round-robin, so id w is the
 // (w / 8)-th workgroup that XCD x = w % 8 runs. When the heads split evenly

@@ -122,23 +122,43 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   // K/V staging: global_load_lds_dwordx4 writes lane i's 16 bytes to LDS at
   // the wave's base + 16 i, so each lane fetches the global chunk that
-  // belongs at its LDS slot under the XOR swizzle. Rows past N are clamped
-  // to row N-1: their keys are masked, so only finiteness of the data matters.
+  // belongs at its LDS slot under the XOR swizzle. The byte offsets of those
+  // chunks within a tile are the same for every tile, so they are computed
+  // once; the tile's first row is a wave-uniform base. In a last, partial
+  // tile, rows past N are clamped to row N-1: their keys are masked, so only
+  // finiteness of the data matters.
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  unsigned koff[CPT], voff[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int p = (wvu * CPT + j) * 64 + lane;
+    const int row = p / CPR;
+    koff[j] = row * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4);
+    voff[j] = row * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4);
+  }
   auto dma = [&](int t, int buf) {
     const int k0 = t * BC;
+    const char* gK = (const char*)K + (size_t)k0 * ROWB;
+    const char* gV = (const char*)V + (size_t)k0 * ROWB;
     char* sK = smem + buf * TILEB;
     char* sV = smem + (2 + buf) * TILEB;
+    if (k0 + BC <= N) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int slot = (wv * CPT + j) * 64;  // first LDS chunk of this instruction
-      const int p = slot + lane;
-      const int row = p / CPR;
-      int gr = k0 + row;
-      gr = gr < N ? gr : N - 1;
-      const int ck = (p % CPR) ^ swz_k16<D>(row);
-      const int cv = (p % CPR) ^ swz_v16<D>(row);
-      lds_dma16(K + (size_t)gr * D + ck * 8, lds_addr(sK + slot * 16));
-      lds_dma16(V + (size_t)gr * D + cv * 8, lds_addr(sV + slot * 16));
+      for (int j = 0; j < CPT; ++j) {
+        const int slot = (wvu * CPT + j) * 64;  // first LDS chunk of this instruction
+        lds_dma16_s(gK, koff[j], lds_addr(sK + slot * 16));
+        lds_dma16_s(gV, voff[j], lds_addr(sV + slot * 16));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int slot = (wvu * CPT + j) * 64;
+        const int p = slot + lane;
+        const int row = p / CPR;
+        const int gr = min(row, N - 1 - k0);
+        lds_dma16_s(gK, gr * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4), lds_addr(sK + slot * 16));
+        lds_dma16_s(gV, gr * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4), lds_addr(sV + slot * 16));
+      }
     }
   };
 
@@ -184,6 +204,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         }
       };
       kread(0, 0);
+      // the first chunk's reads stand alone, so that every group below pairs
+      // the reads of chunk kc + 1 with the MFMAs of chunk kc
+      __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         if (kc + 1 < KC) kread(kc + 1, (kc + 1) & 1);
@@ -412,19 +435,42 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
                        : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
   const int q_lo_key = MASK == MASK_LOCAL ? qi - a.window : 0;
 
-  // direct global->LDS copy of key tile t into buffer buf (K) and 2 + buf (V)
-  auto dma = [&](int t, int buf) {
+  // direct global->LDS copy of key tile t into buffer buf (K) and 2 + buf (V):
+  // per-lane byte offsets within a tile computed once, the tile's first row
+  // as a wave-uniform base; rows past N (last tile only) read row N-1, as
+  // their keys are masked
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  unsigned koff[CPW], voff[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int slot = (wv * CPW + i) * 64;
-      const int p = slot + lane;
-      const int row = p / CPR;
-      int gr = t * BC + row;
-      gr = gr < N ? gr : N - 1;  // keys past N are masked
-      const int ck = (p % CPR) ^ swz_k16<D>(row);
-      const int cv = (p % CPR) ^ swz_v16<D>(row);
-      lds_dma16(K + (size_t)gr * D + ck * 8, lds_addr(smem + buf * TILEB + slot * 16));
-      lds_dma16(V + (size_t)gr * D + cv * 8, lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+  for (int i = 0; i < CPW; ++i) {
+    const int p = (wvu * CPW + i) * 64 + lane;
+    const int row = p / CPR;
+    koff[i] = row * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4);
+    voff[i] = row * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4);
+  }
+  auto dma = [&](int t, int buf) {
+    const int k0 = t * BC;
+    const char* gK = (const char*)K + (size_t)k0 * ROWB;
+    const char* gV = (const char*)V + (size_t)k0 * ROWB;
+    if (k0 + BC <= N) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int slot = (wvu * CPW + i) * 64;
+        lds_dma16_s(gK, koff[i], lds_addr(smem + buf * TILEB + slot * 16));
+        lds_dma16_s(gV, voff[i], lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int slot = (wvu * CPW + i) * 64;
+        const int p = slot + lane;
+        const int row = p / CPR;
+        const int gr = min(row, N - 1 - k0);
+        lds_dma16_s(gK, gr * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4),
+                    lds_addr(smem + buf * TILEB + slot * 16));
+        lds_dma16_s(gV, gr * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4),
+                    lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+      }
     }
   };
 
