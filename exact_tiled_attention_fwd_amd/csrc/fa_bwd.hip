@@ -269,6 +269,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       const bool need_mask = !tile_full<MASK>(qr0, qr0 + 32, kw0, kw0 + 32, a.window);
+      if (need_mask) {  // a uniform branch: full tiles run no per-element compare
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!allowed<MASK>(qr0 + 8 * (r >> 2) + 4 * h + (r & 3), key, a.window)) sa[r] = -INFINITY;
+      }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const f32x4 L4 = *(const f32x4*)&sL[buf][qb * 32 + 8 * rr + 4 * h];
@@ -276,8 +281,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
-          float sv = sa[r];
-          if (need_mask && !allowed<MASK>(qr0 + 8 * rr + 4 * h + e, key, a.window)) sv = -INFINITY;
+          const float sv = sa[r];
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -L4[e]));
           sa[r] = pv;
           dp[r] = pv * (dp[r] - D4[e]);
@@ -441,8 +445,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int tr_row = 4 * h + (s16 >> 2);
   const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
+  // the tile loop unrolled by two, so that the double-buffer index is a
+  // compile-time constant (LDS addresses take it as an immediate offset)
+  auto tile_step = [&](int t, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
     if (t + 1 < t_end) dma(t + 1, buf ^ 1);
@@ -478,14 +484,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
         const int kb0 = k0 + kb * 32;
         const bool need_mask =
             (kb0 + 32 > N) || !tile_full<MASK>(qw0, qw0 + 32, kb0, kb0 + 32, a.window);
+        if (need_mask) {  // a uniform branch: full tiles run no per-element compare
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = kb0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (!(kk < N && allowed<MASK>(qi, kk, a.window))) sa[r] = -INFINITY;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float sv = sa[r];
-          if (need_mask) {
-            const int kk = kb0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (!(kk < N && allowed<MASK>(qi, kk, a.window))) sv = -INFINITY;
-          }
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -Lq));
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -Lq));
           sa[r] = pv * (dp[r] - Dq);
         }
 #pragma unroll
@@ -509,6 +517,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed in LDS
     __syncthreads();
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    tile_step(t, ic<0>{});
+    if (t + 1 < t_end) tile_step(t + 1, ic<1>{});
   }
 
   if (qi < N) {

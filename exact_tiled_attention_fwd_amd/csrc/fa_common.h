@@ -65,6 +65,12 @@ __device__ __forceinline__ void wg_tile(int w, int BH, int ntiles, int& bh, int&
   rank = w - bh * ntiles;
 }
 
+// Compile-time integer tag for generic lambdas.
+template <int V>
+struct ic {
+  static constexpr int value = V;
+};
+
 // Mask modes, mirroring fa_mask.
 enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_LOCAL = 2 };
 

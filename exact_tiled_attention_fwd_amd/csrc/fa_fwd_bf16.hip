@@ -175,8 +175,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int tr_row = 4 * h + (s16 >> 2);
   const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
+  // the tile loop unrolled by two, so that the double-buffer index is a
+  // compile-time constant (LDS addresses take it as an immediate offset)
+  auto tile_step = [&](int t, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
     if (t + 1 < t_end) dma(t + 1, buf ^ 1);
@@ -335,6 +337,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
     __syncthreads();
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    tile_step(t, ic<0>{});
+    if (t + 1 < t_end) tile_step(t + 1, ic<1>{});
   }
 
   // ---- epilogue: O = acc / l, LSE = m * scale + ln l
@@ -359,11 +365,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-// Compile-time integer tag for generic lambdas.
-template <int V>
-struct ic {
-  static constexpr int value = V;
-};
 
 // ---------------------------------------------------------------------------
 // Block-pipelined variant. The online softmax runs per 32-key block (the
