@@ -91,7 +91,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sVt[BC * ROWB];      // V rows of this workgroup
   __shared__ __attribute__((aligned(16))) char sQO[4 * QTILEB];     // Q[2], dO[2]
   __shared__ __attribute__((aligned(16))) float sL[2][BRQ];         // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][BRQ];         // D
+  __shared__ __attribute__((aligned(16))) float sD[2][BRQ];         // -D
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
   auto st_stats = [&](int buf) {
     if (tid < BRQ) {
       sL[buf][tid] = stL;
-      sD[buf][tid] = stD;
+      sD[buf][tid] = -stD;
     }
   };
 
@@ -241,11 +241,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
       if (!(wave_live && qr0 < wq_hi && qr0 + 32 > wq_lo)) continue;  // no allowed pair
       // S = Q K^T and dP = dO V^T (lane <-> key, 16 query rows); operands
       // read one 16-wide chunk ahead
+      // dP starts from -D (its 16 query rows): the MFMAs then produce dP - D,
+      // the factor that dS = P (dP - D) needs, with no subtraction
       f32x16 sa, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sa[r] = 0.f;
-        dp[r] = 0.f;
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 nD4 = *(const f32x4*)&sD[buf][qb * 32 + 8 * rr + 4 * h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sa[4 * rr + e] = 0.f;
+          dp[4 * rr + e] = nD4[e];
+        }
       }
       const int arow = qb * 32 + l32;
       bf16x8 qa[2], oa[2], va[2];
@@ -277,14 +283,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const f32x4 L4 = *(const f32x4*)&sL[buf][qb * 32 + 8 * rr + 4 * h];
-        const f32x4 D4 = *(const f32x4*)&sD[buf][qb * 32 + 8 * rr + 4 * h];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
-          const float sv = sa[r];
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -L4[e]));
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -L4[e]));
           sa[r] = pv;
-          dp[r] = pv * (dp[r] - D4[e]);
+          dp[r] = pv * dp[r];
         }
       }
       // dV += P^T dO and dK += dS^T Q; B operands by transposed reads
@@ -380,7 +384,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     oop[kc] = __builtin_bit_cast(bf16x8, y);
   }
   const float Lq = qi < N ? a.lse[(size_t)bh * N + qi] * 1.4426950408889634f : INFINITY;
+  // dP^T starts from -D_i (this lane's query): the MFMAs then produce
+  // dP - D, the factor that dS = P (dP - D) needs, with no subtraction
   const float Dq = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  f32x16 negD;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negD[r] = -Dq;
   const float c = a.scale_log2;
 
   f32x16 dq[DT];
@@ -457,12 +466,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
       bf16x8 dsb[KB][2];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        f32x16 sa, dp;
+        f32x16 sa, dp = negD;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sa[r] = 0.f;
-          dp[r] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r) sa[r] = 0.f;
         const int arow = kb * 32 + l32;
         bf16x8 ka[2], va[2];
         auto rd = [&](int kc, int sl) {
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -Lq));
-          sa[r] = pv * (dp[r] - Dq);
+          sa[r] = pv * dp[r];
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
