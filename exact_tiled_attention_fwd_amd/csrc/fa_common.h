@@ -21,6 +21,13 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(FA_LDS const char*)p;
 }
 
+// The copies below set M0 (the LDS destination of global_load_lds_*) inside
+// their assembly. The kernels keep no value of their own in M0 (none of their
+// LDS instructions reads it), so the compiler's note that a clobbered reserved
+// register may not be preserved across the statement does not apply.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane i's chunk lands at lds_base + 16 i, lds_base wave-uniform (M0).
 // Issued as inline assembly so that the compiler does not make later LDS
@@ -42,6 +49,8 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, un
                : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // Workgroup id -> (head, tile rank); rank 0 is launched first.
 // Workgroup ids are handed to the eight XCDs round-robin, so id w is the

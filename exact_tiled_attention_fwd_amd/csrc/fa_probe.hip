@@ -73,15 +73,15 @@ fa_status timed(hipStream_t s, F launch, float* ms) {
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return FA_ERR_LAUNCH;
   if (hipEventCreate(&e1) != hipSuccess) {
-    hipEventDestroy(e0);
+    (void)hipEventDestroy(e0);
     return FA_ERR_LAUNCH;
   }
   fa_status st = FA_OK;
   if (hipEventRecord(e0, s) != hipSuccess || !launch() || hipEventRecord(e1, s) != hipSuccess ||
       hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(ms, e0, e1) != hipSuccess)
     st = FA_ERR_LAUNCH;
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   return st;
 }
 
