@@ -9,23 +9,26 @@
 //   dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j
 // where LSE is the forward's saved log-sum-exp.
 //
-// Three launches on the caller's stream, no atomics, deterministic:
-//  1. preprocess: D_i for every row (reads O and dO once).
+// Two launches on the caller's stream (bf16), no atomics, deterministic:
+//  1. dQ, query-major (the forward's layout): S^T = K Q^T and dP^T = V dO^T
+//     put the query on the lane, so LSE_i and D_i are per-lane scalars, and
+//     dS^T is the B operand of dQ^T += K^T dS^T (K read transposed). Each
+//     query row belongs to one wave, which also computes D_i from its dO and
+//     O rows and stores it in the workspace.
 //  2. dK/dV, key-major: a workgroup owns a block of keys (K in registers and
 //     V in LDS as MFMA B operands) and streams every query tile that sees
-//     them through LDS. S = Q K^T puts the key on the lane, so P^T and dS^T
-//     are already the A operands of dV += P^T dO and dK += dS^T Q; the B
-//     operands (dO, Q with the query along the lane vector) come from
-//     ds_read_b64_tr_b16.
-//  3. dQ, query-major (the forward's layout): S^T = K Q^T and dP^T = V dO^T
-//     put the query on the lane, so LSE_i and D_i are per-lane scalars, and
-//     dS^T is the B operand of dQ^T += K^T dS^T (K read transposed).
-// Recomputing S and dP in step 3 costs two extra contractions (7 instead of
-// the 5 the gradient needs), the price of determinism without atomics.
+//     them (Q, dO, LSE, D) through LDS. S = Q K^T puts the key on the lane,
+//     so P^T and dS^T are already the A operands of dV += P^T dO and
+//     dK += dS^T Q; the B operands (dO, Q with the query along the lane
+//     vector) come from ds_read_b64_tr_b16.
+// Recomputing S and dP in the dQ kernel costs two extra contractions (7
+// instead of the 5 the gradient needs), the price of determinism without
+// atomics. The float32 path keeps a separate preprocess launch for D.
 #include <stdlib.h>
 
 #include "fa_common.h"
 #include "fa_kernels.h"
+#include "fa_tile_ops.h"
 
 namespace fa {
 
@@ -41,27 +44,6 @@ __device__ __forceinline__ int swz_dual(int row) {
   }
 }
 
-
-// ---------------------------------------------------------------- preprocess
-// D_i = <dO_i, O_i> in float32; d/8 threads per row, 16 bytes each.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const bf16* __restrict__ o,
-                                                           const bf16* __restrict__ dout,
-                                                           float* __restrict__ delta, long rows) {
-  constexpr int TPR = D / 8;
-  const long row = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 x = *(const bf16x8*)(o + row * D + part * 8);
-    const bf16x8 y = *(const bf16x8*)(dout + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && part == 0) delta[row] = acc;
-}
 
 // ------------------------------------------------------------------ dK / dV
 // dK/dV, key-major: NW waves (two per SIMD) of 32 keys each. To fit two
@@ -384,9 +366,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     oop[kc] = __builtin_bit_cast(bf16x8, y);
   }
   const float Lq = qi < N ? a.lse[(size_t)bh * N + qi] * 1.4426950408889634f : INFINITY;
+  // D_i = <dO_i, O_i>, the row term of dS = P (dP - D). This kernel owns
+  // every query row once, so it computes D_i here (lanes l and l + 32 hold
+  // the two halves of row l) and stores it for the dK/dV kernel, which runs
+  // after it on the stream.
+  const bf16* __restrict__ Op = (const bf16*)a.o + base;
+  float dpart = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (qi < N) z = *(const u32x4*)(Op + (size_t)qi * D + kc * 16 + h * 8);
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, z);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)ov[e], (float)oop[kc][e], dpart);
+  }
+  const float Dq = pair_sum(dpart);
+  if (h == 0 && qi < N) a.delta[(size_t)bh * N + qi] = Dq;
   // dP^T starts from -D_i (this lane's query): the MFMAs then produce
   // dP - D, the factor that dS = P (dP - D) needs, with no subtraction
-  const float Dq = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
   f32x16 negD;
 #pragma unroll
   for (int r = 0; r < 16; ++r) negD[r] = -Dq;
@@ -685,25 +682,20 @@ __global__ __launch_bounds__(F32B_T) void bwd_dq_f32_kernel(BwdArgs a) {
 // dK/dV (KNW waves of 32 keys) and dQ (QNW waves of 32 queries) launches.
 template <int D, int MASK, int KNW, int QNW>
 static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
-  const int n_kt = (a.N + KNW * 32 - 1) / (KNW * 32);
-  hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<D, KNW, 32, MASK>), dim3((unsigned)(n_kt * a.BH)),
-                     dim3(KNW * 64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // dQ first: it also writes D, which the dK/dV kernel reads
   const int n_qt = (a.N + QNW * 32 - 1) / (QNW * 32);
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, QNW, 64, MASK>), dim3((unsigned)(n_qt * a.BH)),
                      dim3(QNW * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_kt = (a.N + KNW * 32 - 1) / (KNW * 32);
+  hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<D, KNW, 32, MASK>), dim3((unsigned)(n_kt * a.BH)),
+                     dim3(KNW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int MASK>
 static hipError_t launch_bwd_bf16_mask(const BwdArgs& a, int cfg, hipStream_t stream) {
-  const long rows = (long)a.BH * a.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
-                     0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // Under a band mask a wave needs only the query (key) rows within the
   // window of its own 32 keys (queries), while a workgroup streams the union
   // over its waves: four waves per workgroup keep more of each streamed tile

@@ -1,6 +1,7 @@
-// Device helpers shared by the forward kernels (query-major and key-major):
-// LDS swizzles of K/V tiles, the lane-pair reductions of the transposed score
-// layout, and the max / sum trees over one 32-key accumulator block.
+// Device helpers shared by the forward kernels (query-major and key-major)
+// and the query-major dQ kernel: LDS swizzles of K/V tiles, the lane-pair
+// reductions of the transposed score layout, and the max / sum trees over one
+// 32-key accumulator block.
 #pragma once
 #include "fa_common.h"
 
