@@ -311,6 +311,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
       // read first, then its PV MFMAs share a scheduling region with the exp /
       // convert VALU work of block kb (a few VALU ops per MFMA), so LDS
       // latency, the matrix core and the vector ALU overlap.
+      // Two waves share each SIMD (wave w and w + NW/2); the older one wins
+      // issue arbitration, finishes its tile first and then idles at the
+      // barrier while the younger one runs alone. From its exponentials to
+      // the end of the tile the younger wave takes priority instead.
+      if (NW == 8 && wvu >= NW / 2) __builtin_amdgcn_s_setprio(1);
       exp_block(0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -333,6 +338,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb];
+      if (NW == 8 && wvu >= NW / 2) __builtin_amdgcn_s_setprio(0);
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
