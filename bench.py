@@ -116,11 +116,11 @@ def _pmc_per_dispatch(path, counter):
     return {n: sum(v) / len(v) for n, v in out.items()}
 
 
-def summarize_pmc(d, copy_mib):
+def summarize_pmc(d, copy_mib, workload):
     """Markdown summary of the FETCH_SIZE / WRITE_SIZE passes in directory d:
-    bench run (fetch_*, write_*) and the copy calibration (copy_fetch_*,
-    copy_write_*). Counter readings are scaled so that the plain copy of
-    copy_mib MiB reads and writes exactly that many bytes."""
+    bench run on `workload` (fetch_*, write_*) and the copy calibration
+    (copy_fetch_*, copy_write_*). Counter readings are scaled so that the
+    plain copy of copy_mib MiB reads and writes exactly that many bytes."""
     one = lambda pat: sorted(glob.glob(os.path.join(d, pat)))[0]
     cf = _pmc_per_dispatch(one("copy_fetch*_counter_collection.csv"), "FETCH_SIZE")
     cw = _pmc_per_dispatch(one("copy_write*_counter_collection.csv"), "WRITE_SIZE")
@@ -146,7 +146,8 @@ def summarize_pmc(d, copy_mib):
     for name, f_, w_, rb, wb in rows:
         short = re.sub(r"\(.*", "", name)
         lines.append(f"| `{short}` | {f_:.0f} | {w_:.0f} | {rb / 1e6:.1f} MB | {wb / 1e6:.1f} MB |")
-    meta = {"source_sha": kernel_source_sha(), "fetch_factor": round(f_fetch, 4),
+    meta = {"source_sha": kernel_source_sha(), "workload": workload,
+            "fetch_factor": round(f_fetch, 4),
             "write_factor": round(f_write, 4),
             "units": {u: {k: round(v) for k, v in x.items()} for u, x in units.items()}}
     lines += ["", f"Calibration: the {copy_mib} MiB copy (`{ck}`) reads {cf[ck]:.0f} KiB and writes "
@@ -159,9 +160,10 @@ def summarize_pmc(d, copy_mib):
     return "\n".join(lines)
 
 
-def load_traffic(unit):
-    """HBM bytes per call of `unit` from the committed counter summary, or
-    None when the summary was taken on different kernel sources."""
+def load_traffic(unit, workload):
+    """HBM bytes per call of `unit` on `workload` from a committed counter
+    summary, or None when none was taken on this workload with the current
+    kernel sources."""
     sha = kernel_source_sha()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as f:
@@ -170,7 +172,8 @@ def load_traffic(unit):
         if not m:
             continue
         meta = json.loads(m.group(1))
-        if meta.get("source_sha") == sha and unit in meta.get("units", {}):
+        if (meta.get("source_sha") == sha and meta.get("workload") == workload
+                and unit in meta.get("units", {})):
             x = meta["units"][unit]
             return int(x["read_bytes"] + x["write_bytes"]), os.path.relpath(path, ROOT)
     return None, None
@@ -219,7 +222,8 @@ def main():
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
     args = ap.parse_args()
     if args.summarize_pmc:
-        print(summarize_pmc(args.summarize_pmc, args.copy_mib))
+        print(summarize_pmc(args.summarize_pmc, args.copy_mib,
+                            args.workload or "bf16_causal_bwd_b2h16_n4096_d128"))
         return
     if args.summarize_std:
         print(summarize_std(args.summarize_std, args.copy_mib))
@@ -337,7 +341,7 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n][0])
     ms_dom, fl_dom, by_dom = kernels[dom]
     achieved = fl_dom / (ms_dom * 1e-3) / 1e12
-    traffic, traffic_src = load_traffic(dom)
+    traffic, traffic_src = load_traffic(dom, w.name)
     # which roof binds: arithmetic intensity against the ridge of the published peaks
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if fl_dom / by_dom >= ridge:
