@@ -2,7 +2,8 @@
 
 This module only draws random tensors and names workload shapes; it holds
 none of the attention arithmetic. Both the GPU parity tests and the CPU
-oracle read the same host tensors produced here.
+oracle read the same host tensors produced here (for multi-GB tensors, the
+same recipe runs on the device and the oracle reads slices copied back).
 
 Recipe: one ``torch.Generator`` per workload seeded with the workload's seed,
 ``torch.randn`` in float32 on the CPU, drawn in the order Q, K, V (then dO);
@@ -93,3 +94,15 @@ def random_inputs(shape, dtype=torch.bfloat16, seed=0, qk_mult=1.0, with_dout=Fa
     if with_dout:
         out["dout"] = torch.randn(shape, generator=g, dtype=torch.float32)
     return {n: t.to(dtype).contiguous() for n, t in out.items()}
+
+
+def device_inputs(shape, dtype=torch.bfloat16, seed=0, with_dout=False, device="cuda"):
+    """The same recipe drawn by a generator on `device`, for tensors too large
+    to draw and copy from the host (several GB each). The values differ from
+    random_inputs with the same seed; a test hands the oracle slices copied
+    back from these tensors."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = {}
+    for n in ("q", "k", "v") + (("dout",) if with_dout else ()):
+        out[n] = torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(dtype)
+    return out
