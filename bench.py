@@ -95,7 +95,8 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-# Entry point each kernel belongs to (one fa_bwd call = three launches).
+# Entry point each kernel belongs to (one bf16 fa_bwd call = two launches, dQ then
+# dK/dV; the float32 path adds a launch for D).
 UNIT_OF_KERNEL = (("fwd_bf16", "fa_fwd"), ("fwd_f32", "fa_fwd"), ("bwd_pre", "fa_bwd"),
                   ("bwd_dkdv", "fa_bwd"), ("bwd_dq", "fa_bwd"))
 TRAFFIC_TAG = "traffic-json:"
