@@ -13,7 +13,8 @@ spell), then the W warm-up steps, then exactly K timed steps between two
 device synchronisations.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       python bench.py --summarize-pmc DIR --copy-mib M   (HBM traffic summary, no GPU)
+       python bench.py --summarize-pmc DIR --copy-mib M [--workload NAME]
+                                      (HBM traffic summary of that workload, no GPU)
        python bench.py --sweep        (N = 2k..16k sweep, markdown table on stdout)
        python bench.py --gemm-ref     (vendor bf16 GEMM rate, for context)
        python bench.py --std-sweep [--std-n N] [--no-settle]
@@ -161,12 +162,13 @@ def summarize_pmc(d, copy_mib, workload):
     return "\n".join(lines)
 
 
-def load_traffic(unit, workload):
+def load_traffic(unit, workload, profiles_dir=None):
     """HBM bytes per call of `unit` on `workload` from a committed counter
     summary, or None when none was taken on this workload with the current
     kernel sources."""
     sha = kernel_source_sha()
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+    pdir = profiles_dir or os.path.join(ROOT, "profiles")
+    for path in sorted(glob.glob(os.path.join(pdir, "*.md"))):
         with open(path) as f:
             text = f.read()
         m = re.search(re.escape(TRAFFIC_TAG) + r"\s*(\{.*\})\s*-->", text)
@@ -236,7 +238,7 @@ def main():
         print(summarize_util(args.summarize_util))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (heads shard across GPUs without "
+        print("bench.py: runs on one GPU only (heads shard across GPUs without "
               "communication, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
