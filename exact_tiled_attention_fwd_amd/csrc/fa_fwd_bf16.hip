@@ -28,7 +28,7 @@
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
 //  * Two schedules: the tile kernel runs all scores of a K tile, then the
 //    softmax, then P V with the exp of the next 32-key block interleaved;
-//    the block-pipelined kernel (used at d = 64) overlaps the scores of
+//    the block-pipelined kernel (an alternative) overlaps the scores of
 //    block b+1 with the exp of block b and P V of block b with the maximum
 //    of block b+1, keeping the online-softmax state per 32-key block.
 //  * The subtracted maximum is refreshed lazily: the reference m only moves
@@ -680,11 +680,16 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
 
 // Kernel choice per head dimension, picked by interleaved timing on MI355X
 // (causal 8192 x 128, 4096 x 128, unmasked 2048 x 64, band 16384 x 128):
-// d = 128 uses the tile kernel with 128-key tiles, d = 64 the block-pipelined
-// kernel with 64-key tiles. Under a band mask a wave needs only the key tiles
-// within the window of its 32 rows while the workgroup streams the union over
-// its waves, so d = 128 bands use four-wave workgroups with 64-key tiles
-// (two per CU): 218 -> 174 us on [1, 32, 16384, 128] with radius 128.
+// d = 128 uses the tile kernel with 128-key tiles. d = 64 uses the tile
+// kernel with two 32-row query blocks per wave (each K and V operand read
+// feeds two MFMAs), four-wave workgroups (two per CU) and 64-key tiles:
+// against the block-pipelined kernel 82.2 -> 78.8 us on [4, 16, 2048, 64],
+// 316 -> 302 us on [16, 16, 2048, 64], 602 -> 577 us on causal
+// [4, 16, 8192, 64]; at d = 128 two blocks per wave do not fit the registers.
+// Under a band mask a wave needs only the key tiles within the window of its
+// rows while the workgroup streams the union over its waves, so d = 128
+// bands use four-wave workgroups with 64-key tiles (two per CU):
+// 218 -> 174 us on [1, 32, 16384, 128] with radius 128.
 // cfg selects the alternatives for timing sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
@@ -703,7 +708,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
     case 2: return launch_fwd_bf16_xb<64, 128>(a, mask, stream);
     case 3: return launch_fwd_bf16_cfg<64, 1, 8, 128>(a, mask, stream);
     case 4: return launch_fwd_bf16_cfg<64, 1, 4, 64>(a, mask, stream);
-    default: return launch_fwd_bf16_xb<64, 64>(a, mask, stream);
+    case 5: return launch_fwd_bf16_xb<64, 64>(a, mask, stream);
+    case 6: return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
+    default: return launch_fwd_bf16_cfg<64, 2, 4, 64>(a, mask, stream);
   }
 }
 

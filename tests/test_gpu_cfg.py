@@ -8,9 +8,10 @@ is an untested one.
 
 Forward, d = 128: 1 = tile kernel 8 waves x 64 keys, 2 = block-pipelined
 kernel 128 keys, 3 = block-pipelined 64 keys, 4 = tile kernel 4 waves x 64
-keys. d = 64: 1 = tile kernel 8 x 64, 2 = block-pipelined 128 keys, 3 = tile
-kernel 8 x 128, 4 = tile kernel 4 x 64. Backward: 2 swaps the workgroup size
-(4 or 8 waves) that the mask would otherwise choose.
+keys (5, 6: the default). d = 64: 1 = tile kernel 8 x 64, 2 = block-pipelined
+128 keys, 3 = tile kernel 8 x 128, 4 = tile kernel 4 x 64, 5 = block-pipelined
+64 keys, 6 = tile kernel with two query blocks per wave, 8 x 64. Backward: 2
+swaps the workgroup size (4 or 8 waves) that the mask would otherwise choose.
 """
 import pytest
 
@@ -31,7 +32,7 @@ FWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("cfg", ["1", "2", "3", "4", "5", "6"])
 @pytest.mark.parametrize("shape,mask,window,mult", FWD_CASES,
                          ids=[f"{s}-{m}-{w}-x{k:g}" for s, m, w, k in FWD_CASES])
 def test_fwd_cfg(monkeypatch, cfg, shape, mask, window, mult):
