@@ -249,7 +249,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    fa.load()  # fail loudly if the HIP library is missing
+    fa._native.ensure_built()  # compiles only when no library is there
+    fa.load()  # fail loudly if the HIP library is still missing
     dev = torch.device("cuda", 0)
 
     if args.copy_probe_mib:

@@ -30,6 +30,15 @@ class FAError(RuntimeError):
         super().__init__(f"{where}: {fa_status_string(status)}")
 
 
+def ensure_built():
+    """Compile libfa.so (hipcc, gfx950) if it is not there yet; an existing
+    library is used as it is. For the test suite, the smoke check and the
+    bench; load() itself never builds and fails when the library is missing."""
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+
+
 def load():
     """Load libfa.so (raises OSError if it has not been built)."""
     global _lib

@@ -26,8 +26,7 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_native.LIB_PATH):
-        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    _native.ensure_built()
     return _native.load()
 
 
