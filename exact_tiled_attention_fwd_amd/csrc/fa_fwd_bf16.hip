@@ -691,8 +691,10 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
 // registers.
 // Under a band mask a wave needs only the key tiles within the window of its
 // rows while the workgroup streams the union over its waves, so d = 128
-// bands use four-wave workgroups with 64-key tiles (two per CU):
-// 218 -> 174 us on [1, 32, 16384, 128] with radius 128.
+// bands use four-wave workgroups: 218 -> 174 us on [1, 32, 16384, 128] with
+// radius 128 (64-key tiles, two per CU). With 32-key tiles the kernel needs
+// 158 VGPRs, so three waves share each SIMD, which hides more of the band's
+// memory latency: 163 -> 156 and 158.6 -> 154.3 us on two cards.
 // cfg selects the alternatives for timing sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
@@ -702,7 +704,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
       case 3: return launch_fwd_bf16_xb<128, 64>(a, mask, stream);
       case 4: return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
       default:
-        if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
+        if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<128, 1, 4, 32>(a, mask, stream);
         return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
     }
   }

@@ -8,7 +8,7 @@ is an untested one.
 
 Forward, d = 128: 1 = tile kernel 8 waves x 64 keys, 2 = block-pipelined
 kernel 128 keys, 3 = block-pipelined 64 keys, 4 = tile kernel 4 waves x 64
-keys (5, 6: the default). d = 64: 1 = tile kernel 8 x 64, 2 = block-pipelined
+keys (the band default is 4 waves x 32 keys; 5, 6: the default). d = 64: 1 = tile kernel 8 x 64, 2 = block-pipelined
 128 keys, 3 = tile kernel 8 x 128, 4 = tile kernel 4 x 64, 5 = block-pipelined
 64 keys, 6 = the two-block tile kernel at the other workgroup size (4 or 8
 waves) than the mask would choose. Backward: 2
