@@ -694,7 +694,9 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
 // bands use four-wave workgroups: 218 -> 174 us on [1, 32, 16384, 128] with
 // radius 128 (64-key tiles, two per CU). With 32-key tiles the kernel needs
 // 158 VGPRs, so three waves share each SIMD, which hides more of the band's
-// memory latency: 163 -> 156 and 158.6 -> 154.3 us on two cards.
+// memory latency: 163 -> 156 and 158.6 -> 154.3 us on two cards. At d = 64
+// the band takes one query block per wave and 32-key tiles (100 VGPRs, five
+// waves per SIMD): 112 -> 76 us on [1, 32, 16384, 64] with radius 128.
 // cfg selects the alternatives for timing sweeps.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
@@ -719,6 +721,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
       return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
     default:
       if (mask == MASK_NONE) return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
+      if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<64, 1, 4, 32>(a, mask, stream);
       return launch_fwd_bf16_cfg<64, 2, 4, 64>(a, mask, stream);
   }
 }
