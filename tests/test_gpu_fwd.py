@@ -49,6 +49,9 @@ SMALL = [
     ((1, 2, 1000, 64), "causal", 0),
     ((1, 2, 777, 64), "local", 64),
     ((3, 5, 65, 64), "local", 3),
+    ((1, 2, 700, 64), "local", 0),
+    ((1, 1, 600, 64), "local", 5000),
+    ((1, 2, 1000, 64), "local", 128),
 ]
 
 
