@@ -18,7 +18,9 @@ FA_F32, FA_BF16 = 0, 1
 MASK_CODES = {None: 0, "none": 0, "causal": 1, "local": 2}
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
                 4: "FA_ERR_HEADDIM", 5: "FA_ERR_MASK", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIGN",
-                8: "FA_ERR_WORKSPACE", 9: "FA_ERR_LAUNCH", 10: "FA_ERR_ALIAS"}
+                8: "FA_ERR_WORKSPACE", 9: "FA_ERR_LAUNCH", 10: "FA_ERR_ALIAS",
+                11: "FA_ERR_CONFIG"}
+I32_MAX = 2 ** 31 - 1
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string")
 
 _lib = None
@@ -54,6 +56,11 @@ def load():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_fwd_tuned.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_tuned.restype = i
+    lib.fa_bwd_tuned.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                 i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_bwd_tuned.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
@@ -95,6 +102,17 @@ def _mask_code(mask) -> int:
     return MASK_CODES[mask]
 
 
+def _window(window) -> int:
+    """The band radius as the C int the library takes: radii past 2^31 - 1
+    allow the same pairs as 2^31 - 1 (every |i - j| is below N), negative ones
+    stay negative (the library rejects them under the band mask), so no value
+    wraps around."""
+    w = int(window)
+    if w > I32_MAX:
+        return I32_MAX
+    return max(w, -1)
+
+
 def _check(name, t, ref=None, dtype=None, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -122,9 +140,7 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def fa_fwd(q, k, v, o, lse, scale, mask=None, window=0, stream=None):
-    """Call fa_fwd on [B, H, N, d] tensors q, k, v -> o (same dtype) and
-    lse [B, H, N] float32, enqueued on `stream` (default: torch's current)."""
+def _fwd_args(q, k, v, o, lse):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
@@ -132,11 +148,29 @@ def fa_fwd(q, k, v, o, lse, scale, mask=None, window=0, stream=None):
     for n, t in (("k", k), ("v", v), ("o", o)):
         _check(n, t, q, q.dtype, q.shape)
     _check("lse", lse, q, torch.float32, (B, H, N))
+    return B, H, N, d
+
+
+def fa_fwd(q, k, v, o, lse, scale, mask=None, window=0, stream=None):
+    """Call fa_fwd on [B, H, N, d] tensors q, k, v -> o (same dtype) and
+    lse [B, H, N] float32, enqueued on `stream` (default: torch's current)."""
+    B, H, N, d = _fwd_args(q, k, v, o, lse)
     st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       B, H, N, d, _dtype_code(q), float(scale), _mask_code(mask), int(window),
-                       _stream(q, stream))
+                       B, H, N, d, _dtype_code(q), float(scale), _mask_code(mask),
+                       _window(window), _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_fwd")
+
+
+def fa_fwd_tuned(q, k, v, o, lse, scale, mask=None, window=0, cfg=0, stream=None):
+    """Call fa_fwd_tuned (include/fa_tuning.h): fa_fwd with the alternative
+    kernel shape `cfg` (0 = the default shape)."""
+    B, H, N, d = _fwd_args(q, k, v, o, lse)
+    st = load().fa_fwd_tuned(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), B, H, N, d, _dtype_code(q), float(scale),
+                             _mask_code(mask), _window(window), int(cfg), _stream(q, stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd_tuned")
 
 
 def fa_fwd_standard_workspace_bytes(B, H, N, d, dtype) -> int:
@@ -159,7 +193,7 @@ def fa_fwd_standard(q, k, v, o, lse, workspace, scale, mask=None, window=0, stre
     wbytes = workspace.numel() * workspace.element_size()
     st = load().fa_fwd_standard(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 lse.data_ptr(), workspace.data_ptr(), wbytes, B, H, N, d,
-                                _dtype_code(q), float(scale), _mask_code(mask), int(window),
+                                _dtype_code(q), float(scale), _mask_code(mask), _window(window),
                                 _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_fwd_standard")
@@ -186,7 +220,7 @@ def fa_fwd_keymajor(q, k, v, o, lse, workspace, scale, mask=None, window=0, bloc
     wbytes = workspace.numel() * workspace.element_size()
     st = load().fa_fwd_keymajor(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 lse.data_ptr(), workspace.data_ptr(), wbytes, B, H, N, d,
-                                _dtype_code(q), float(scale), _mask_code(mask), int(window),
+                                _dtype_code(q), float(scale), _mask_code(mask), _window(window),
                                 int(block_keys), _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_fwd_keymajor")
@@ -197,11 +231,7 @@ def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
     return int(load().fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d), code))
 
 
-def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, window=0,
-           stream=None):
-    """Call fa_bwd: gradients dq, dk, dv (same dtype/shape as q) from
-    q, k, v, o, dout and lse; `workspace` is a uint8 GPU tensor of at least
-    fa_bwd_workspace_bytes(...) bytes."""
+def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
@@ -209,14 +239,39 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, windo
     for n, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check(n, t, q, q.dtype, q.shape)
     _check("lse", lse, q, torch.float32, (B, H, N))
+    return B, H, N, d
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, window=0,
+           stream=None):
+    """Call fa_bwd: gradients dq, dk, dv (same dtype/shape as q) from
+    q, k, v, o, dout and lse; `workspace` is a uint8 GPU tensor of at least
+    fa_bwd_workspace_bytes(...) bytes."""
+    B, H, N, d = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv)
     _check("workspace", workspace, q)
     wbytes = workspace.numel() * workspace.element_size()
     st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                        workspace.data_ptr(), wbytes, B, H, N, d, _dtype_code(q), float(scale),
-                       _mask_code(mask), int(window), _stream(q, stream))
+                       _mask_code(mask), _window(window), _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_bwd")
+
+
+def fa_bwd_tuned(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, window=0,
+                 cfg=0, stream=None):
+    """Call fa_bwd_tuned (include/fa_tuning.h): fa_bwd with the alternative
+    kernel shape `cfg` (0 = the default shape)."""
+    B, H, N, d = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv)
+    _check("workspace", workspace, q)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = load().fa_bwd_tuned(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), workspace.data_ptr(), wbytes, B, H, N, d,
+                             _dtype_code(q), float(scale), _mask_code(mask), _window(window),
+                             int(cfg), _stream(q, stream))
+    if st != 0:
+        raise FAError(st, "fa_bwd_tuned")
 
 
 def fa_probe_mfma_bf16(iters, stream=None) -> float:

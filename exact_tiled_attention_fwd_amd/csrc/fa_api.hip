@@ -6,61 +6,69 @@
 #include <stdlib.h>
 
 #include "fa.h"
+#include "fa_host.h"
 #include "fa_kernels.h"
+
+using namespace fa::host;
 
 namespace {
 
-constexpr int64_t kI32Max = 2147483647;
+// Kernel choice of the forward: 0 is the measured default; other values
+// select the alternative shapes kept for timing comparisons (fa_tuning.h).
+constexpr int kFwdCfgMax = 8;
 
-size_t elem_bytes(fa_dtype dt) { return dt == FA_BF16 ? 2 : 4; }
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// [a, a+na) and [b, b+nb) overlap.
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
+void set_scale(const ScaleFold& f, fa::FwdArgs& a) {
+  a.scale_abs = f.scale_abs;
+  a.scale_log2 = f.scale_log2;
+  a.q_and = f.q_and;
+  a.q_xor = f.q_xor;
 }
 
-fa_status check_problem(int B, int H, int N, int d, fa_dtype dtype, float scale, fa_mask mask,
-                        int window) {
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if ((int64_t)B * H > kI32Max) return FA_ERR_SHAPE;
-  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
-  if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (dtype == FA_F32 && (d < 1 || d > 128)) return FA_ERR_HEADDIM;
-  if ((int64_t)N * d > kI32Max) return FA_ERR_SHAPE;
-  // one workgroup per 32 query rows at most, per head
-  if (((int64_t)N + 31) / 32 * ((int64_t)B * H) > kI32Max) return FA_ERR_SHAPE;
-  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_LOCAL) return FA_ERR_MASK;
-  if (mask == FA_MASK_LOCAL && window < 0) return FA_ERR_MASK;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  return FA_OK;
-}
-
-int tuning_cfg(const char* name) {
-  const char* s = getenv(name);
-  return s ? atoi(s) : 0;
-}
-
-// Sign handling of the scale for the bf16 kernels: the kernel's exp2
-// argument needs a positive factor, so a negative scale negates Q (exact in
-// bf16) and a zero (or underflowing) scale zeroes Q, which makes every logit
-// exactly 0 as scale = 0 does.
-void bf16_scale(float scale, fa::FwdArgs& a) {
-  const double LOG2E = 1.4426950408889634;
-  double s = fabs((double)scale);
-  a.q_and = 0xFFFFFFFFu;
-  a.q_xor = scale < 0 ? 0x80008000u : 0u;
-  float c = (float)(s * LOG2E);
-  if (!(c >= 1.17549435e-38f)) {  // zero, or too small for a normal float factor
-    a.q_and = 0u;
-    a.q_xor = 0u;
-    s = 1.0;
-    c = (float)LOG2E;
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, fa_dtype dtype, float scale, fa_mask mask, int window, int cfg,
+                   void* stream) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) ||
+      overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) ||
+      overlap(o, tb, lse, lb))
+    return FA_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == FA_BF16) {
+    fa::FwdArgs a;
+    a.q = (const bf16*)q;
+    a.k = (const bf16*)k;
+    a.v = (const bf16*)v;
+    a.o = (bf16*)o;
+    a.lse = lse;
+    a.BH = B * H;
+    a.N = N;
+    a.n_qtiles = 0;
+    a.window = kernel_window(mask, window, N);
+    set_scale(fold_scale(scale), a);
+    e = fa::launch_fwd_bf16(a, d, (int)mask, cfg, s);
+  } else {
+    if (cfg != 0) return FA_ERR_CONFIG;
+    fa::FwdF32Args a;
+    a.q = (const float*)q;
+    a.k = (const float*)k;
+    a.v = (const float*)v;
+    a.o = (float*)o;
+    a.lse = lse;
+    a.BH = B * H;
+    a.N = N;
+    a.d = d;
+    a.window = kernel_window(mask, window, N);
+    a.scale = scale;
+    e = fa::launch_fwd_f32(a, (int)mask, s);
   }
-  a.scale_abs = (float)s;
-  a.scale_log2 = c;
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -80,6 +88,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input";
+    case FA_ERR_CONFIG: return "FA_ERR_CONFIG: unknown kernel configuration";
   }
   return "unknown fa_status";
 }
@@ -87,48 +96,14 @@ const char* fa_status_string(fa_status s) {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, fa_dtype dtype, float scale, fa_mask mask, int window,
                  void* stream) {
-  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
-  if (st != FA_OK) return st;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_ERR_ALIGN;
-  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) ||
-      overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) ||
-      overlap(o, tb, lse, lb))
-    return FA_ERR_ALIAS;
-  if (mask != FA_MASK_LOCAL) window = 0;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (dtype == FA_BF16) {
-    fa::FwdArgs a;
-    a.q = (const bf16*)q;
-    a.k = (const bf16*)k;
-    a.v = (const bf16*)v;
-    a.o = (bf16*)o;
-    a.lse = lse;
-    a.BH = B * H;
-    a.N = N;
-    a.n_qtiles = 0;
-    a.window = window;
-    bf16_scale(scale, a);
-    e = fa::launch_fwd_bf16(a, d, (int)mask, tuning_cfg("FA_FWD_CFG"), s);
-  } else {
-    fa::FwdF32Args a;
-    a.q = (const float*)q;
-    a.k = (const float*)k;
-    a.v = (const float*)v;
-    a.o = (float*)o;
-    a.lse = lse;
-    a.BH = B * H;
-    a.N = N;
-    a.d = d;
-    a.window = window;
-    a.scale = scale;
-    e = fa::launch_fwd_f32(a, (int)mask, s);
-  }
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, dtype, scale, mask, window, 0, stream);
+}
+
+fa_status fa_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int N, int d, fa_dtype dtype, float scale, fa_mask mask, int window,
+                       int cfg, void* stream) {
+  if (cfg < 0 || cfg > kFwdCfgMax) return FA_ERR_CONFIG;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, dtype, scale, mask, window, cfg, stream);
 }
 
 // Standard (unfused) attention: workspace = S (float32, rows padded to 4)
@@ -184,7 +159,7 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
   a.N = N;
   a.lds = (N + 3) & ~3;
   a.ldp = (N + 7) & ~7;
-  a.window = mask == FA_MASK_LOCAL ? window : 0;
+  a.window = kernel_window(mask, window, N);
   a.scale = scale;
   const hipError_t e = fa::launch_std_bf16(a, d, (int)mask, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -220,8 +195,7 @@ fa_status fa_fwd_keymajor(const void* q, const void* k, const void* v, void* o, 
       return FA_ERR_ALIAS;
   if (overlap(o, tb, lse, lb) || overlap(workspace, total, o, tb) || overlap(workspace, total, lse, lb))
     return FA_ERR_ALIAS;
-  fa::FwdArgs f;
-  bf16_scale(scale, f);
+  const ScaleFold f = fold_scale(scale);
   fa::KmArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -232,7 +206,7 @@ fa_status fa_fwd_keymajor(const void* q, const void* k, const void* v, void* o, 
   a.BH = B * H;
   a.N = N;
   a.n_qtiles = 0;
-  a.window = mask == FA_MASK_LOCAL ? window : 0;
+  a.window = kernel_window(mask, window, N);
   a.scale_log2 = f.scale_log2;
   a.scale_abs = f.scale_abs;
   a.q_and = f.q_and;

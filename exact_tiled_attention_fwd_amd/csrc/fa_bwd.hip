@@ -24,8 +24,6 @@
 // Recomputing S and dP in the dQ kernel costs two extra contractions (7
 // instead of the 5 the gradient needs), the price of determinism without
 // atomics. The float32 path keeps a separate preprocess launch for D.
-#include <stdlib.h>
-
 #include "fa_common.h"
 #include "fa_kernels.h"
 #include "fa_tile_ops.h"
@@ -722,10 +720,8 @@ static hipError_t launch_bwd_f32_mask(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int MASK>
-static hipError_t launch_bwd_mask(const BwdArgs& a, int bf16_path, hipStream_t stream) {
+static hipError_t launch_bwd_mask(const BwdArgs& a, int bf16_path, int cfg, hipStream_t stream) {
   if (bf16_path) {
-    const char* env = getenv("FA_BWD_CFG");  // tuning only: 2 swaps the workgroup size choice
-    const int cfg = env ? atoi(env) : 0;
     if (a.d == 128) return launch_bwd_bf16_mask<128, MASK>(a, cfg, stream);
     return launch_bwd_bf16_mask<64, MASK>(a, cfg, stream);
   }
@@ -735,11 +731,11 @@ static hipError_t launch_bwd_mask(const BwdArgs& a, int bf16_path, hipStream_t s
   return launch_bwd_f32_mask<128, MASK>(a, stream);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int bf16_path, int mask, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int bf16_path, int mask, int cfg, hipStream_t stream) {
   switch (mask) {
-    case MASK_CAUSAL: return launch_bwd_mask<MASK_CAUSAL>(a, bf16_path, stream);
-    case MASK_LOCAL: return launch_bwd_mask<MASK_LOCAL>(a, bf16_path, stream);
-    default: return launch_bwd_mask<MASK_NONE>(a, bf16_path, stream);
+    case MASK_CAUSAL: return launch_bwd_mask<MASK_CAUSAL>(a, bf16_path, cfg, stream);
+    case MASK_LOCAL: return launch_bwd_mask<MASK_LOCAL>(a, bf16_path, cfg, stream);
+    default: return launch_bwd_mask<MASK_NONE>(a, bf16_path, cfg, stream);
   }
 }
 

@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_host.h"
 #include "fa_kernels.h"
 
 namespace fa {
@@ -14,23 +15,72 @@ size_t bwd_workspace_bytes(int BH, int N) { return round256((size_t)BH * N * siz
 
 }  // namespace fa
 
+using namespace fa::host;
+
 namespace {
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
+// Kernel choice of the backward: 0 is the measured default, 2 the other
+// workgroup size (fa_tuning.h).
+bool bwd_cfg_ok(int cfg) { return cfg == 0 || cfg == 2; }
+
+// Validation of everything but the workspace, and the kernel arguments.
+fa_status bwd_prepare(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, const void* workspace,
+                      size_t ws_bytes, int B, int H, int N, int d, fa_dtype dtype, float scale,
+                      fa_mask mask, int window, fa::BwdArgs& a) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const void* ins[] = {q, k, v, o, dout};
+  void* outs[] = {dq, dk, dv};
+  for (void* out : outs) {
+    for (const void* in : ins)
+      if (overlap(out, tb, in, tb)) return FA_ERR_ALIAS;
+    if (overlap(out, tb, lse, lb)) return FA_ERR_ALIAS;
+    if (workspace && overlap(out, tb, workspace, ws_bytes)) return FA_ERR_ALIAS;
+  }
+  if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
+    return FA_ERR_ALIAS;
+  if (workspace) {
+    for (const void* in : ins)
+      if (overlap(workspace, ws_bytes, in, tb)) return FA_ERR_ALIAS;
+    if (overlap(workspace, ws_bytes, lse, lb)) return FA_ERR_ALIAS;
+  }
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.delta = (float*)workspace;
+  a.BH = B * H;
+  a.N = N;
+  a.d = d;
+  a.window = kernel_window(mask, window, N);
+  a.scale = scale;
+  const ScaleFold f = fold_scale(scale);
+  a.scale_abs = f.scale_abs;
+  a.scale_log2 = f.scale_log2;
+  a.q_and = f.q_and;
+  a.q_xor = f.q_xor;
+  return FA_OK;
 }
 
-fa_status check_problem(int B, int H, int N, int d, fa_dtype dtype) {
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if ((int64_t)B * H > 2147483647) return FA_ERR_SHAPE;
-  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
-  if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (dtype == FA_F32 && (d < 1 || d > 128)) return FA_ERR_HEADDIM;
-  if ((int64_t)N * d > 2147483647) return FA_ERR_SHAPE;
-  if (((int64_t)N + 31) / 32 * ((int64_t)B * H) > 2147483647) return FA_ERR_SHAPE;
-  return FA_OK;
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int H, int N, int d, fa_dtype dtype, float scale,
+                   fa_mask mask, int window, int cfg, void* stream) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
+  if (st != FA_OK) return st;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N);
+  fa::BwdArgs a;
+  st = bwd_prepare(q, k, v, o, dout, lse, dq, dk, dv, workspace, need, B, H, N, d, dtype, scale,
+                   mask, window, a);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, (int)mask, cfg, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -38,7 +88,7 @@ fa_status check_problem(int B, int H, int N, int d, fa_dtype dtype) {
 extern "C" {
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
-  if (check_problem(B, H, N, d, dtype) != FA_OK) return 0;
+  if (check_problem(B, H, N, d, dtype, 1.0f, FA_MASK_NONE, 0) != FA_OK) return 0;
   return fa::bwd_workspace_bytes(B * H, N);
 }
 
@@ -46,58 +96,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, int B, int H, int N, int d, fa_dtype dtype, float scale,
                  fa_mask mask, int window, void* stream) {
-  fa_status st = check_problem(B, H, N, d, dtype);
-  if (st != FA_OK) return st;
-  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL && mask != FA_MASK_LOCAL) return FA_ERR_MASK;
-  if (mask == FA_MASK_LOCAL && window < 0) return FA_ERR_MASK;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes(B * H, N);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t tb = (size_t)B * H * N * d * (dtype == FA_BF16 ? 2 : 4);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const void* ins[] = {q, k, v, o, dout};
-  void* outs[] = {dq, dk, dv};
-  for (void* out : outs) {
-    for (const void* in : ins)
-      if (overlap(out, tb, in, tb)) return FA_ERR_ALIAS;
-    if (overlap(out, tb, lse, lb) || overlap(out, tb, workspace, need)) return FA_ERR_ALIAS;
-  }
-  if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
-    return FA_ERR_ALIAS;
-  for (const void* in : ins)
-    if (overlap(workspace, need, in, tb)) return FA_ERR_ALIAS;
-  if (overlap(workspace, need, lse, lb)) return FA_ERR_ALIAS;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                  dtype, scale, mask, window, 0, stream);
+}
 
-  fa::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv;
-  a.delta = (float*)workspace;
-  a.BH = B * H;
-  a.N = N;
-  a.d = d;
-  a.window = mask == FA_MASK_LOCAL ? window : 0;
-  a.scale = scale;
-  {
-    const double LOG2E = 1.4426950408889634;
-    double s = fabs((double)scale);
-    a.q_and = 0xFFFFFFFFu;
-    a.q_xor = scale < 0 ? 0x80008000u : 0u;
-    float c = (float)(s * LOG2E);
-    if (!(c >= 1.17549435e-38f)) {
-      a.q_and = 0u;
-      a.q_xor = 0u;
-      s = 1.0;
-      c = (float)LOG2E;
-    }
-    a.scale_abs = (float)s;
-    a.scale_log2 = c;
-  }
-  hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, (int)mask, (hipStream_t)stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+fa_status fa_bwd_tuned(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       fa_dtype dtype, float scale, fa_mask mask, int window, int cfg,
+                       void* stream) {
+  if (!bwd_cfg_ok(cfg) || (cfg != 0 && dtype != FA_BF16)) return FA_ERR_CONFIG;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                  dtype, scale, mask, window, cfg, stream);
 }
 
 }  // extern "C"

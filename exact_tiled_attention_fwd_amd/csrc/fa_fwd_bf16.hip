@@ -44,8 +44,10 @@ namespace fa {
 
 
 
-template <int D, int QB, int NW, int BC, int MASK>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+// WPE: waves per SIMD the register budget is sized for (2: 256 registers per
+// lane; 1: 512, for workgroups whose LDS use leaves room for one per CU).
+template <int D, int QB, int NW, int BC, int MASK, int WPE = 2>
+__global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QW = QB * 32;       // query rows per wave
   constexpr int BR = NW * QW;       // query rows per workgroup
@@ -146,8 +148,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int slot = (wvu * CPT + j) * 64;  // first LDS chunk of this instruction
-        lds_dma16_s(gK, koff[j], lds_addr(sK + slot * 16));
-        lds_dma16_s(gV, voff[j], lds_addr(sV + slot * 16));
+        if constexpr (BC <= 128) {
+          lds_dma16_s(gK, koff[j], lds_addr(sK + slot * 16));
+          lds_dma16_s(gV, voff[j], lds_addr(sV + slot * 16));
+        } else {
+          // tiles longer than 128 keys leave too few scalar registers for the
+          // base-plus-offset form: full per-lane addresses instead
+          lds_dma16(gK + koff[j], lds_addr(sK + slot * 16));
+          lds_dma16(gV + voff[j], lds_addr(sV + slot * 16));
+        }
       }
     } else {
 #pragma unroll
@@ -156,8 +165,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         const int p = slot + lane;
         const int row = p / CPR;
         const int gr = min(row, N - 1 - k0);
-        lds_dma16_s(gK, gr * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4), lds_addr(sK + slot * 16));
-        lds_dma16_s(gV, gr * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4), lds_addr(sV + slot * 16));
+        const unsigned ko = gr * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4);
+        const unsigned vo = gr * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4);
+        if constexpr (BC <= 128) {
+          lds_dma16_s(gK, ko, lds_addr(sK + slot * 16));
+          lds_dma16_s(gV, vo, lds_addr(sV + slot * 16));
+        } else {
+          lds_dma16(gK + ko, lds_addr(sK + slot * 16));
+          lds_dma16(gV + vo, lds_addr(sV + slot * 16));
+        }
       }
     }
   };
@@ -463,8 +479,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
         const int slot = (wvu * CPW + i) * 64;
-        lds_dma16_s(gK, koff[i], lds_addr(smem + buf * TILEB + slot * 16));
-        lds_dma16_s(gV, voff[i], lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+        if constexpr (BC <= 128) {
+          lds_dma16_s(gK, koff[i], lds_addr(smem + buf * TILEB + slot * 16));
+          lds_dma16_s(gV, voff[i], lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+        } else {
+          // the longer unrolled block loop of these tiles leaves too few
+          // scalar registers for the base-plus-offset form: full per-lane
+          // addresses instead
+          lds_dma16(gK + koff[i], lds_addr(smem + buf * TILEB + slot * 16));
+          lds_dma16(gV + voff[i], lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+        }
       }
     } else {
 #pragma unroll
@@ -473,10 +497,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
         const int p = slot + lane;
         const int row = p / CPR;
         const int gr = min(row, N - 1 - k0);
-        lds_dma16_s(gK, gr * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4),
-                    lds_addr(smem + buf * TILEB + slot * 16));
-        lds_dma16_s(gV, gr * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4),
-                    lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+        const unsigned ko = gr * ROWB + (((p % CPR) ^ swz_k16<D>(row)) << 4);
+        const unsigned vo = gr * ROWB + (((p % CPR) ^ swz_v16<D>(row)) << 4);
+        if constexpr (BC <= 128) {
+          lds_dma16_s(gK, ko, lds_addr(smem + buf * TILEB + slot * 16));
+          lds_dma16_s(gV, vo, lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+        } else {
+          lds_dma16(gK + ko, lds_addr(smem + buf * TILEB + slot * 16));
+          lds_dma16(gV + vo, lds_addr(smem + (2 + buf) * TILEB + slot * 16));
+        }
       }
     }
   };
@@ -664,16 +693,16 @@ static hipError_t launch_fwd_bf16_xb(const FwdArgs& a0, int mask, hipStream_t st
   return hipGetLastError();
 }
 
-template <int D, int QB, int NW, int BC>
+template <int D, int QB, int NW, int BC, int WPE = 2>
 static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t stream) {
   FwdArgs a = a0;
   constexpr int BR = NW * QB * 32;
   a.n_qtiles = (a.N + BR - 1) / BR;
   dim3 grid((unsigned)(a.n_qtiles * a.BH)), block(NW * 64);
   switch (mask) {
-    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
-    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_NONE>), grid, block, 0, stream, a); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_CAUSAL, WPE>), grid, block, 0, stream, a); break;
+    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_LOCAL, WPE>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW, BC, MASK_NONE, WPE>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }
@@ -697,7 +726,15 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
 // memory latency: 163 -> 156 and 158.6 -> 154.3 us on two cards. At d = 64
 // the band takes one query block per wave and 32-key tiles (100 VGPRs, five
 // waves per SIMD): 112 -> 76 us on [1, 32, 16384, 64] with radius 128.
-// cfg selects the alternatives for timing sweeps.
+// cfg selects the alternatives for timing comparisons. cfg 7 and 8 are the
+// tile that "What the tiling is actually constrained by" derives from the
+// on-chip memory ("The formula, which the title only gestures at"):
+// B_c = ceil(M / 4d) keys with M = 160 KiB of LDS counted in bf16 elements
+// (160 at d = 128, 320 at d = 64; double-buffered K and V then fill the LDS
+// exactly) and B_r = min(B_c, d) rows (128, 64). cfg 7 takes both literally
+// in the tile kernel (one workgroup per compute unit, so one wave per SIMD
+// with the register file to itself); cfg 8 keeps B_c in the block-pipelined
+// kernel, whose live score registers do not grow with the tile, at 256 rows.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream) {
   if (d == 128) {
     switch (cfg) {
@@ -705,6 +742,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
       case 2: return launch_fwd_bf16_xb<128, 128>(a, mask, stream);
       case 3: return launch_fwd_bf16_xb<128, 64>(a, mask, stream);
       case 4: return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
+      case 7: return launch_fwd_bf16_cfg<128, 1, 4, 160, 1>(a, mask, stream);
+      case 8: return launch_fwd_bf16_xb<128, 160>(a, mask, stream);
       default:
         if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<128, 1, 4, 32>(a, mask, stream);
         return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
@@ -719,6 +758,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
     case 6:  // the other workgroup size of the default
       if (mask == MASK_NONE) return launch_fwd_bf16_cfg<64, 2, 4, 64>(a, mask, stream);
       return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
+    case 7: return launch_fwd_bf16_cfg<64, 1, 2, 320, 1>(a, mask, stream);
+    case 8: return launch_fwd_bf16_xb<64, 320>(a, mask, stream);
     default:
       if (mask == MASK_NONE) return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
       if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<64, 1, 4, 32>(a, mask, stream);

@@ -105,6 +105,7 @@ struct BwdArgs {
 // Workspace layout shared by fa_bwd_workspace_bytes and the launcher.
 size_t bwd_workspace_bytes(int BH, int N);
 
-hipError_t launch_bwd(const BwdArgs& a, int bf16, int mask, hipStream_t stream);
+// cfg selects an alternative workgroup size (0 = default); tuning only.
+hipError_t launch_bwd(const BwdArgs& a, int bf16, int mask, int cfg, hipStream_t stream);
 
 }  // namespace fa

@@ -33,7 +33,9 @@
  *    errors are reported before anything is enqueued; a launch failure is
  *    reported as FA_ERR_LAUNCH; faults during execution surface at the
  *    caller's next synchronization.
- *  - Limits: B, H, N >= 1; B*H <= 2^31-1; N*d <= 2^31-1.
+ *  - Limits: B, H, N >= 1; B*H <= 2^31-1; N <= 2^29; N*d <= 2^31-1.
+ *    Any window >= N - 1 allows every pair of a sequence (the band then
+ *    equals no mask); windows up to 2^31 - 1 are accepted.
  */
 #ifndef FA_H
 #define FA_H
@@ -55,7 +57,8 @@ typedef enum {
     FA_ERR_ALIGN = 7,     /* a pointer is not 16-byte aligned */
     FA_ERR_WORKSPACE = 8, /* workspace missing or smaller than required */
     FA_ERR_LAUNCH = 9,    /* the HIP runtime rejected a kernel launch */
-    FA_ERR_ALIAS = 10     /* an output buffer overlaps an input buffer */
+    FA_ERR_ALIAS = 10,    /* an output buffer overlaps an input buffer */
+    FA_ERR_CONFIG = 11    /* unknown kernel configuration (fa_tuning.h only) */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;

@@ -62,6 +62,7 @@ def test_fwd_argument_errors(lib):
     assert fwd(lib, q=ctypes.c_void_p(0x100004)) == 7  # FA_ERR_ALIGN
     assert fwd(lib, o=FAKE) == 10                     # output aliases an input
     assert fwd(lib, N=1 << 30, d=128) == 2           # N * d beyond 2^31 - 1
+    assert fwd(lib, dtype=0, d=1, N=(1 << 29) + 1) == 2  # N beyond 2^29
 
 
 def test_bwd_argument_errors(lib):
@@ -130,3 +131,29 @@ def test_keymajor_workspace_and_errors(lib):
     assert call(dtype=0) == 3
     assert call(ws=None) == 8 and call(wb=100) == 8
     assert call(ws=ctypes.c_void_p(0x4000004)) == 7
+
+
+def test_tuned_entry_points_reject_unknown_cfg(lib):
+    """fa_fwd_tuned / fa_bwd_tuned check cfg before anything else
+    (FA_ERR_CONFIG = 11), and a float32 call takes only cfg 0."""
+    o, lse = ctypes.c_void_p(0x200000), ctypes.c_void_p(0x900000)
+    def tf(cfg, dtype=1, d=64, q=FAKE):
+        return lib.fa_fwd_tuned(q, FAKE, FAKE, o, lse, 1, 1, 8, d, dtype, 0.125, 0, 0, cfg, None)
+    assert tf(-1) == 11 and tf(9) == 11 and tf(1 << 20) == 11
+    assert tf(3, dtype=0, d=8) == 11
+    assert tf(0, q=None) == 1 and tf(5, q=None) == 1  # a known cfg goes on to validation
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    def tb(cfg, dtype=1):
+        return lib.fa_bwd_tuned(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], p[9], 1 << 20,
+                                1, 1, 8, 64, dtype, 0.125, 0, 0, cfg, None)
+    assert tb(1) == 11 and tb(3) == 11 and tb(2, dtype=0) == 11
+    assert _native.fa_status_string(11).startswith("FA_ERR_CONFIG")
+
+
+def test_window_marshalling():
+    """Radii are passed as C ints without wrapping: above 2^31 - 1 they are
+    passed as 2^31 - 1 (the same pairs), below -1 as -1 (still rejected)."""
+    assert _native._window(0) == 0 and _native._window(128) == 128
+    assert _native._window(2 ** 31 - 1) == 2 ** 31 - 1
+    assert _native._window(2 ** 31) == 2 ** 31 - 1 and _native._window(2 ** 63) == 2 ** 31 - 1
+    assert _native._window(-1) == -1 and _native._window(-(2 ** 32) + 5) == -1

@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle
-from exact_tiled_attention_fwd_amd import attention_bwd, attention_fwd, fa_bwd, FAError
+from exact_tiled_attention_fwd_amd import (attention_bwd, attention_fwd, fa_bwd, fa_bwd_tuned,
+                                           fa_bwd_workspace_bytes, FAError)
 from exact_tiled_attention_fwd_amd.synth import WORKLOADS, make_inputs, random_inputs
 from tests import gpu_util as G
 
@@ -23,15 +24,24 @@ def rel(g, ref):
     return float(np.linalg.norm(g - ref) / (n if n > 0 else 1.0))
 
 
-def run_case(shape, dtype, mask, window, scale=None, seed=0, qk_mult=1.0):
+def run_case(shape, dtype, mask, window, scale=None, seed=0, qk_mult=1.0, cfg=0):
+    """fa_fwd then fa_bwd (or, with cfg != 0, fa_bwd_tuned with that kernel
+    shape) on seeded inputs against the oracle's dense backward."""
     B, H, N, d = shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     inp = random_inputs(shape, dtype, seed=seed, qk_mult=qk_mult, with_dout=True)
     q, k, v, do = (G.to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
-    print(f"bwd case shape={shape} dtype={dtype} mask={mask} w={window} scale={scale}", flush=True)
+    print(f"bwd case shape={shape} dtype={dtype} mask={mask} w={window} scale={scale} cfg={cfg}",
+          flush=True)
     o, lse = attention_fwd(q, k, v, scale, mask, window)
-    dq, dk, dv = attention_bwd(q, k, v, o, lse, do, scale, mask, window)
+    if cfg:
+        ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d, q.dtype), dtype=torch.uint8,
+                         device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        fa_bwd_tuned(q, k, v, o, do, lse, dq, dk, dv, ws, scale, mask, window, cfg)
+    else:
+        dq, dk, dv = attention_bwd(q, k, v, o, lse, do, scale, mask, window)
     torch.cuda.synchronize()
     ref = oracle.bwd_dense(inp["q"], inp["k"], inp["v"], inp["dout"], scale, mask, window)
     errs = {}

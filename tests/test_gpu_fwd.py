@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from exact_tiled_attention_fwd_amd import fa_fwd, attention_fwd, FAError
+from exact_tiled_attention_fwd_amd import fa_fwd, fa_fwd_tuned, attention_fwd, FAError
 from exact_tiled_attention_fwd_amd.synth import WORKLOADS, make_inputs, random_inputs
 from tests import gpu_util as G
 
@@ -16,14 +16,22 @@ pytestmark = pytest.mark.gpu
 BF16, F32 = torch.bfloat16, torch.float32
 
 
-def run_case(shape, dtype, mask, window, scale=None, qk_mult=1.0, seed=0):
+def run_case(shape, dtype, mask, window, scale=None, qk_mult=1.0, seed=0, cfg=0):
+    """fa_fwd (or, with cfg != 0, fa_fwd_tuned with that kernel shape) on
+    seeded inputs against the dense oracle, element by element."""
     B, H, N, d = shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     inp = random_inputs(shape, dtype, seed=seed, qk_mult=qk_mult)
     q, k, v = (G.to_dev(inp[n]) for n in ("q", "k", "v"))
-    print(f"case shape={shape} dtype={dtype} mask={mask} w={window} scale={scale}", flush=True)
-    o, lse = attention_fwd(q, k, v, scale, mask, window)
+    print(f"case shape={shape} dtype={dtype} mask={mask} w={window} scale={scale} cfg={cfg}",
+          flush=True)
+    if cfg:
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+        fa_fwd_tuned(q, k, v, o, lse, scale, mask, window, cfg)
+    else:
+        o, lse = attention_fwd(q, k, v, scale, mask, window)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.fwd_dense(inp["q"], inp["k"], inp["v"], scale, mask, window)
     return G.check_fwd(o, lse, o_ref, lse_ref, dtype, f"{shape} {mask} {window}")
