@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--summarize-util", default=None,
                     help="summarize unit-utilization counter passes (MfmaUtil, VALUBusy, LdsUtil, "
                          "...) in DIR per kernel (no GPU)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="every forward kernel shape (fa_fwd_tuned cfg 0..8) on the causal "
+                         "[2,16,8192,128] and unmasked [4,16,2048,64] workloads; markdown table")
     ap.add_argument("--sweep", action="store_true",
                     help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
@@ -258,6 +261,9 @@ def main():
         return
     if args.sweep:
         sweep(torch, fa, dev, args)
+        return
+    if args.tile_sweep:
+        tile_sweep(torch, fa, dev, args)
         return
     if args.gemm_ref:
         gemm_ref(torch, dev)
@@ -490,6 +496,61 @@ def sweep(torch, fa, dev, args):
                           f"{100 * tf / peaks['mfma_bf16_tflops']:.1f} | "
                           f"{nbytes / (ms * 1e-3) / 1e9:.0f} |", flush=True)
                 del q, k, v, do, o, lse, dq, dk, dv, ws
+
+
+# Forward kernel shapes of fa_fwd_tuned (include/fa_tuning.h), per head dim:
+# (cfg, query rows per wave x waves, keys per tile, kernel). cfg 5 and 6 at
+# d = 128 are the default again and are not repeated.
+TILE_CFGS = {
+    128: [(0, "32 x 8", 128, "tile (default)"), (1, "32 x 8", 64, "tile"),
+          (2, "32 x 8", 128, "block-pipelined"), (3, "32 x 8", 64, "block-pipelined"),
+          (4, "32 x 4", 64, "tile"), (7, "32 x 4", 160, "tile, derived B_c and B_r"),
+          (8, "32 x 8", 160, "block-pipelined, derived B_c")],
+    64: [(0, "64 x 8", 64, "tile, two blocks per wave (default)"), (1, "32 x 8", 64, "tile"),
+         (2, "32 x 8", 128, "block-pipelined"), (3, "32 x 8", 128, "tile"),
+         (4, "32 x 4", 64, "tile"), (5, "32 x 8", 64, "block-pipelined"),
+         (6, "64 x 4", 64, "tile, two blocks per wave"),
+         (7, "32 x 2", 320, "tile, derived B_c and B_r"),
+         (8, "32 x 8", 320, "block-pipelined, derived B_c")],
+}
+
+
+def tile_sweep(torch, fa, dev, args):
+    """Every forward kernel shape on the causal [2,16,8192,128] workload and
+    the unmasked [4,16,2048,64] one (seeded inputs of those workloads): each
+    shape runs back to back for 0.2 s (clock settle), then K launches timed
+    with events on the launch stream. Under rocprofv3 --kernel-trace each
+    shape is a kernel of its own name, so the trace gives the same table."""
+    from exact_tiled_attention_fwd_amd.synth import WORKLOADS, make_inputs
+    stream = torch.cuda.current_stream(dev)
+    reps = max(args.steps, 5)
+    print("| workload | cfg | rows per wave x waves | keys per tile | kernel | µs | TFLOP/s | "
+          "% of 2516.6 |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name in ("bf16_causal_b2h16_n8192_d128", "bf16_b4h16_n2048_d64"):
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        for cfg, rows, bc, kern in TILE_CFGS[w.d]:
+            fn = lambda: fa.fa_fwd_tuned(q, k, v, o, lse, w.scale, w.mask, w.window, cfg, stream)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.2:
+                fn()
+                torch.cuda.synchronize()
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record(stream)
+            for _ in range(reps):
+                fn()
+            e_.record(stream)
+            e_.synchronize()
+            ms = s_.elapsed_time(e_) / reps
+            tf = fwd_flops(w) / (ms * 1e-3) / 1e12
+            print(f"| {name} | {cfg} | {rows} | {bc} | {kern} | {ms * 1e3:.1f} | {tf:.1f} | "
+                  f"{100 * tf / PEAK_BF16_TFLOPS:.1f} |", flush=True)
+        del q, k, v, o, lse
 
 
 def time_unit(torch, fn, stream, scratch, reps, settle=True):
