@@ -56,6 +56,8 @@ def load():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_fwd_tuned.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.fa_fwd_tuned.restype = i
     lib.fa_bwd_tuned.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -256,6 +258,22 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, windo
                        _mask_code(mask), _window(window), _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_bwd")
+
+
+FA_BWD_NOALLOC_MAX_ROWS = 1 << 24
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale, mask=None, window=0, stream=None):
+    """Call fa_bwd_noalloc: fa_bwd without a workspace (the library's static
+    device array holds D; B*H*N <= FA_BWD_NOALLOC_MAX_ROWS). Calls that can
+    overlap on one GPU race."""
+    B, H, N, d = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv)
+    st = load().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), B, H, N, d, _dtype_code(q), float(scale),
+                               _mask_code(mask), _window(window), _stream(q, stream))
+    if st != 0:
+        raise FAError(st, "fa_bwd_noalloc")
 
 
 def fa_bwd_tuned(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, mask=None, window=0,

@@ -2,6 +2,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_host.h"
 #include "fa_kernels.h"
@@ -83,9 +85,57 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// ---- allocation-free variant: D in a static device array
+// Every GPU the library runs on holds one copy of `scratch` (64 MiB) until the
+// process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: host code uses only the per-device address that
+// hipGetSymbolAddress returns, taken once per device with that device current.
+constexpr size_t kNoallocRows = FA_BWD_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[kNoallocRows];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+fa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return FA_ERR_LAUNCH;
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, fa_dtype dtype, float scale, fa_mask mask,
+                         int window, void* stream) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, mask, window);
+  if (st != FA_OK) return st;
+  if ((size_t)B * H * N > kNoallocRows) return FA_ERR_WORKSPACE;
+  fa::BwdArgs a;
+  st = bwd_prepare(q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, B, H, N, d, dtype, scale, mask,
+                   window, a);
+  if (st != FA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != FA_OK) return st;
+  // D is written for every row (by the dQ kernel, or the float32 pre-pass)
+  // before anything reads it, so the array needs no clearing between calls.
+  a.delta = (float*)ws;
+  const hipError_t e = fa::launch_bwd(a, dtype == FA_BF16, (int)mask, 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
   if (check_problem(B, H, N, d, dtype, 1.0f, FA_MASK_NONE, 0) != FA_OK) return 0;

@@ -107,6 +107,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  float scale, fa_mask mask, int window, void* stream);
 
 /*
+ * Backward pass without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory at call time: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc. Same operation, arguments, results and errors as fa_bwd, minus
+ * the workspace: D_i = <dO_i, O_i> goes to a static device array of
+ * FA_BWD_NOALLOC_MAX_ROWS floats (64 MiB) that the library holds on every GPU
+ * it runs on until the process ends.
+ *   B * H * N must not exceed FA_BWD_NOALLOC_MAX_ROWS (else FA_ERR_WORKSPACE,
+ *   before anything is enqueued).
+ *   Every call on one GPU shares that GPU's array: calls that can overlap on
+ *   one GPU (different streams, or different host threads without ordering)
+ *   race and may return wrong gradients; calls ordered on one stream are safe.
+ *   The first call on a device looks up the array's address on that device
+ *   (no allocation); FA_ERR_LAUNCH if that fails.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (1u << 24)
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, fa_dtype dtype,
+                         float scale, fa_mask mask, int window, void* stream);
+
+/*
  * Bytes of device workspace fa_fwd_standard needs: the scores S (float32,
  * B*H*N rows of N rounded up to 4) and the probabilities P (bf16, rows of N
  * rounded up to 8), each region rounded up to 256 bytes. O(B*H*N^2): at
