@@ -220,12 +220,18 @@ int oracle_attn_bwd_dense(const double* q, const double* k, const double* v,
                           const double* dout, double* dq, double* dk, double* dv,
                           int64_t BH, int64_t N, int64_t d, double scale, int mask,
                           int64_t window, double* o, double* lse, double* D) {
+    /* Every sum below runs over its index in increasing order, one running
+     * double per output element; the loops are nested so that the inner loop
+     * walks contiguous memory (a column c, or a block of JB key columns, is
+     * carried along), which changes no sum's order and so no result. */
+    enum { JB = 8 };
     double* P = (double*)malloc((size_t)(N * N) * sizeof(double));
     double* dS = (double*)malloc((size_t)(N * N) * sizeof(double));
     double* Oh = (double*)malloc((size_t)(N * d) * sizeof(double));
     double* Dh = (double*)malloc((size_t)N * sizeof(double));
     if (!P || !dS || !Oh || !Dh) { free(P); free(dS); free(Oh); free(Dh); return -1; }
-    for (int64_t bh = 0; bh < BH; ++bh) {
+    int fail = 0;
+    for (int64_t bh = 0; bh < BH && !fail; ++bh) {
         const size_t off = (size_t)bh * N * d;
         const double *Q = q + off, *K = k + off, *V = v + off, *dO = dout + off;
         /* probabilities, output and D, row by row */
@@ -244,13 +250,15 @@ int oracle_attn_bwd_dense(const double* q, const double* k, const double* v,
             for (int64_t j = 0; j < N; ++j)
                 if (Pi[j] != -INFINITY) l += exp(Pi[j] - m);
             for (int64_t j = 0; j < N; ++j) Pi[j] = (Pi[j] == -INFINITY) ? 0.0 : exp(Pi[j] - m) / l;
-            double Di = 0.0;
-            for (int64_t c = 0; c < d; ++c) {
-                double oc = 0.0;
-                for (int64_t j = 0; j < N; ++j) oc += Pi[j] * V[j * d + c];
-                Oh[i * d + c] = oc;
-                Di += dO[i * d + c] * oc;
+            /* O_i = sum_j P_ij v_j, column c carried along j */
+            double* Oi = Oh + i * d;
+            for (int64_t c = 0; c < d; ++c) Oi[c] = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                const double p = Pi[j];
+                for (int64_t c = 0; c < d; ++c) Oi[c] += p * V[j * d + c];
             }
+            double Di = 0.0;
+            for (int64_t c = 0; c < d; ++c) Di += dO[i * d + c] * Oi[c];
             Dh[i] = Di;
             if (lse) lse[bh * N + i] = m + log(l);
             /* dS row */
@@ -260,31 +268,63 @@ int oracle_attn_bwd_dense(const double* q, const double* k, const double* v,
                 dS[i * N + j] = Pi[j] * (dp - Di);
             }
         }
-        /* dQ_i = scale sum_j dS_ij k_j */
-#pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < N; ++i)
-            for (int64_t c = 0; c < d; ++c) {
-                double s = 0.0;
-                for (int64_t j = 0; j < N; ++j) s += dS[i * N + j] * K[j * d + c];
-                dq[off + i * d + c] = scale * s;
+#pragma omp parallel
+        {
+            double* acc = (double*)malloc((size_t)(d > 0 ? d : 1) * sizeof(double));
+            double* skb = (double*)malloc((size_t)(JB * (d > 0 ? d : 1)) * sizeof(double));
+            double* svb = (double*)malloc((size_t)(JB * (d > 0 ? d : 1)) * sizeof(double));
+            if (!acc || !skb || !svb) {
+#pragma omp atomic write
+                fail = 1;
             }
-        /* dK_j = scale sum_i dS_ij q_i ; dV_j = sum_i P_ij dO_i */
-#pragma omp parallel for schedule(static)
-        for (int64_t j = 0; j < N; ++j)
-            for (int64_t c = 0; c < d; ++c) {
-                double sk = 0.0, sv = 0.0;
-                for (int64_t i = 0; i < N; ++i) {
-                    sk += dS[i * N + j] * Q[i * d + c];
-                    sv += P[i * N + j] * dO[i * d + c];
+            /* dQ_i = scale sum_j dS_ij k_j, column c carried along j */
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < N; ++i) {
+                if (!acc) continue;
+                for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+                for (int64_t j = 0; j < N; ++j) {
+                    const double ds_ij = dS[i * N + j];
+                    for (int64_t c = 0; c < d; ++c) acc[c] += ds_ij * K[j * d + c];
                 }
-                dk[off + j * d + c] = scale * sk;
-                dv[off + j * d + c] = sv;
+                for (int64_t c = 0; c < d; ++c) dq[off + i * d + c] = scale * acc[c];
             }
+            /* dK_j = scale sum_i dS_ij q_i ; dV_j = sum_i P_ij dO_i, for a block
+             * of JB keys at a time, each (key, column) carried along i */
+#pragma omp for schedule(static)
+            for (int64_t j0 = 0; j0 < N; j0 += JB) {
+                if (!skb || !svb) continue;
+                const int64_t nb = (N - j0 < JB) ? N - j0 : JB;
+                for (int64_t t = 0; t < nb * d; ++t) { skb[t] = 0.0; svb[t] = 0.0; }
+                for (int64_t i = 0; i < N; ++i) {
+                    for (int64_t jj = 0; jj < nb; ++jj) {
+                        const int64_t j = j0 + jj;
+                        const double ds_ij = dS[i * N + j];
+                        const double p_ij = P[i * N + j];
+                        double* skj = skb + jj * d;
+                        double* svj = svb + jj * d;
+                        for (int64_t c = 0; c < d; ++c) {
+                            skj[c] += ds_ij * Q[i * d + c];
+                            svj[c] += p_ij * dO[i * d + c];
+                        }
+                    }
+                }
+                for (int64_t jj = 0; jj < nb; ++jj) {
+                    const int64_t j = j0 + jj;
+                    const double* skj = skb + jj * d;
+                    const double* svj = svb + jj * d;
+                    for (int64_t c = 0; c < d; ++c) {
+                        dk[off + j * d + c] = scale * skj[c];
+                        dv[off + j * d + c] = svj[c];
+                    }
+                }
+            }
+            free(acc); free(skb); free(svb);
+        }
         if (o) memcpy(o + off, Oh, (size_t)(N * d) * sizeof(double));
         if (D) memcpy(D + bh * N, Dh, (size_t)N * sizeof(double));
     }
     free(P); free(dS); free(Oh); free(Dh);
-    return 0;
+    return fail ? -1 : 0;
 }
 
 /* Backward for chosen rows, by the same chain-rule definition as

@@ -30,9 +30,11 @@ MUTATIONS = [
      "if (mask == OR_MASK_CAUSAL) return j < i + 1 && j != i;"),
     ("band_asymmetric", "(j - i <= window)", "(j - i <= window + 1)"),
     ("bwd_ds_sign", "dS[i * N + j] = Pi[j] * (dp - Di);", "dS[i * N + j] = Pi[j] * (dp + Di);"),
-    ("bwd_dk_scale_dropped", "dk[off + j * d + c] = scale * sk;", "dk[off + j * d + c] = sk;"),
-    ("bwd_dv_transposed", "sv += P[i * N + j] * dO[i * d + c];", "sv += P[j * N + i] * dO[i * d + c];"),
-    ("bwd_dq_wrong_operand", "s += dS[i * N + j] * K[j * d + c];", "s += dS[i * N + j] * V[j * d + c];"),
+    ("bwd_dk_scale_dropped", "dk[off + j * d + c] = scale * skj[c];",
+     "dk[off + j * d + c] = skj[c];"),
+    ("bwd_dv_transposed", "const double p_ij = P[i * N + j];", "const double p_ij = P[j * N + i];"),
+    ("bwd_dq_wrong_operand", "acc[c] += ds_ij * K[j * d + c];", "acc[c] += ds_ij * V[j * d + c];"),
+    ("bwd_o_wrong_operand", "Oi[c] += p * V[j * d + c];", "Oi[c] += p * K[j * d + c];"),
 ]
 
 
