@@ -395,6 +395,14 @@ def main():
         "probes": {k_: round(v_, 1) for k_, v_ in peaks.items()},
     }
 
+    # The same step with cold caches: each of K launches follows a 512 MiB
+    # device write that evicts L2 and the 256 MB MALL; median of the K.
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    ms_step_fl = flushed_median(torch, step, stream, flush_buf, args.steps)
+    out["flushed"] = {"ms_per_step_median": round(ms_step_fl, 4),
+                      "tflops": round(flops_step / (ms_step_fl * 1e-3) / 1e12, 1),
+                      "reps": args.steps, "flush_bytes": FLUSH_BYTES}
+
     if not args.no_headline:
         def hfwd():
             fa.fa_fwd(hq, hk, hv, ho, hl, hw.scale, hw.mask, hw.window, stream)
@@ -403,16 +411,40 @@ def main():
             hfwd()
         hms = timed(hfwd, args.steps)
         ht = fwd_flops(hw) / (hms * 1e-3) / 1e12
+        hms_fl = flushed_median(torch, hfwd, stream, flush_buf, args.steps)
+        ht_fl = fwd_flops(hw) / (hms_fl * 1e-3) / 1e12
         out["headline_forward"] = {
             "workload": hw.name, "tflops": round(ht, 1),
             "frac_of_peak": round(ht / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(hms * 1e3, 2),
-            "hbm_gbs": round(fwd_bytes(hw) / (hms * 1e-3) / 1e9, 1)}
+            "hbm_gbs": round(fwd_bytes(hw) / (hms * 1e-3) / 1e9, 1),
+            "flushed_median_us": round(hms_fl * 1e3, 2), "flushed_tflops": round(ht_fl, 1),
+            "flushed_frac_of_peak": round(ht_fl / PEAK_BF16_TFLOPS, 4)}
         del hq, hk, hv, ho, hl
+    del flush_buf
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, have_bwd)
 
     print(json.dumps(out), flush=True)
+
+
+FLUSH_BYTES = 512 << 20  # larger than L2 plus the 256 MB MALL
+
+
+def flushed_median(torch, fn, stream, flush_buf, reps):
+    """Median milliseconds of `reps` launches of fn, each preceded by a write
+    of flush_buf (outside the timed span) so that fn starts with cold caches;
+    events on the launch stream around fn only."""
+    times = []
+    for i in range(reps):
+        flush_buf.fill_(i & 255)
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        fn()
+        e_.record(stream)
+        e_.synchronize()
+        times.append(s_.elapsed_time(e_))
+    return statistics.median(times)
 
 
 def measured_peaks(torch, fa, dev, stream):
@@ -676,12 +708,12 @@ KM_BCS = (32, 64, 128, 256)
 def km_bytes(N, bc, B=1, H=16, d=64):
     """Model of the key-major forward's device-memory bytes at bf16 [B,H,N,d]:
     each of the T_c = ceil(N/bc) launches reads all of Q and reads and writes
-    the running state of every row (two lanes x (d/2 + 2) floats); K and V
+    the running state of every row (two lanes x (d/2 + 3) floats); K and V
     are read once per head and launch (L2 serves the other workgroups); the
     finalize pass reads the state once more and writes O and LSE."""
     tc = -(-N // bc)
     rows = B * H * (-(-N // 256)) * 256
-    state = rows * 2 * (d // 2 + 2) * 4
+    state = rows * 2 * (d // 2 + 3) * 4
     per_launch = B * H * N * d * 2 + 2 * state + B * H * bc * d * 2 * 2
     return state + tc * per_launch + state + B * H * N * (d * 2 + 4)
 
@@ -850,31 +882,68 @@ def copy_probe(torch, dev, args):
                       "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(w, inp, have_bwd):
-    """The CPU oracle (plain double C, OpenMP) on one (batch, head) slice of
-    the same workload: dense forward over all rows plus, when the step has a
-    backward, the dense backward of that slice."""
+def cpu_model():
+    """The host CPU's model name (first 'model name' of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def omp_threads():
+    """Threads the OpenMP oracle runs with: OMP_NUM_THREADS when set, else
+    the CPUs this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, inp, have_bwd, target_s=12.0):
+    """The CPU oracle (plain double C, OpenMP), as the tests use it, on
+    consecutive (batch, head) slices of the same workload until about
+    target_s seconds of CPU work: per slice the dense forward, the tiled
+    online forward (128 x 128 tiles) and, when the step has a backward, the
+    dense backward. `value` is the dense forward + dense backward rate, the
+    oracle's counterpart of the GPU step."""
     import oracle
     B, H, N, d = w.shape
     flat = {n: inp[n].reshape(B * H, N, d) for n in ("q", "k", "v", "dout")}
     one = type(w)(**{**w.__dict__, "B": 1, "H": 1})
-    flops_slice = fwd_flops(one) + (bwd_flops(one) if have_bwd else 0.0)
-    # slices one after another until about TARGET_S seconds of CPU work
-    TARGET_S = 12.0
+    t_dense = t_tiled = t_bwd = 0.0
     t0 = time.perf_counter()
     n = 0
-    while n < B * H and (time.perf_counter() - t0) < TARGET_S:
+    while n < B * H and (n == 0 or (time.perf_counter() - t0) < target_s):
         sl = {k_: t[n:n + 1] for k_, t in flat.items()}
+        a = time.perf_counter()
         oracle.fwd_dense(sl["q"], sl["k"], sl["v"], w.scale, w.mask, w.window)
+        b = time.perf_counter()
+        oracle.fwd_tiled(sl["q"], sl["k"], sl["v"], w.scale, 128, 128, w.mask, w.window)
+        c = time.perf_counter()
         if have_bwd:
             oracle.bwd_dense(sl["q"], sl["k"], sl["v"], sl["dout"], w.scale, w.mask, w.window)
+        t_dense += b - a
+        t_tiled += c - b
+        t_bwd += time.perf_counter() - c
         n += 1
-    sec = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(n * flops_slice / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(sec, 2),
+    ff, fb = fwd_flops(one) * n, (bwd_flops(one) * n if have_bwd else 0.0)
+    return {"value": round((ff + fb) / (t_dense + t_bwd) / 1e12, 6), "unit": "TFLOP/s",
+            "cores": omp_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+            "seconds": round(t_dense + t_tiled + t_bwd, 2),
+            "dense_fwd_s": round(t_dense, 6), "dense_fwd_tflops": round(ff / t_dense / 1e12, 6),
+            "tiled_fwd_s": round(t_tiled, 6), "tiled_fwd_tflops": round(ff / t_tiled / 1e12, 6),
+            "dense_bwd_s": round(t_bwd, 6) if have_bwd else None,
+            "dense_bwd_tflops": round(fb / t_bwd / 1e12, 6) if have_bwd else None,
             "sample": f"{n} of {B * H} (b,h) slices [1,1,{N},{d}] of {w.name}: dense forward"
-                      + (" + dense backward" if have_bwd else "") + ", float64"}
+                      + (" + dense backward" if have_bwd else "")
+                      + " (value); tiled forward 128x128 timed beside; float64, OpenMP"}
 
 
 if __name__ == "__main__":

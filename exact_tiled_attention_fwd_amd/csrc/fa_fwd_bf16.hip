@@ -105,11 +105,16 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
-  float m_ref[QB], l_run[QB];  // reference maximum (raw units), lane's part of l
+  // reference maximum (raw units); the lane's part of l (float32 sum of the
+  // weights, for the LSE) and of the sum of the bf16-rounded weights (the
+  // output's normalizer, in four running parts)
+  float m_ref[QB], l_run[QB], lb_run[QB][4];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = -INFINITY;
     l_run[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lb_run[qb][i] = 0.f;
   }
   const float c = a.scale_log2;  // > 0
 
@@ -278,6 +283,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
           m_ref[qb] = m_new;
           l_run[qb] *= alpha;
 #pragma unroll
+          for (int i = 0; i < 4; ++i) lb_run[qb][i] *= alpha;
+#pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
@@ -301,6 +308,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
           for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) pop[qb][kb][u][e] = (bf16)sacc[qb][kb][8 * u + e];
+          sum_bf16x16_4(pop[qb][kb], lb_run[qb]);
         }
       };
       // O^T += V^T P^T for one 32-key block; each V read feeds QB MFMAs.
@@ -365,13 +373,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 < t_end) tile_step(t + 1, ic<1>{});
   }
 
-  // ---- epilogue: O = acc / l, LSE = m * scale + ln l
+  // ---- epilogue: O = acc / (sum of the rounded weights), LSE = m * scale + ln l
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = pair_sum(l_run[qb]);
+    const float lbt = pair_sum((lb_run[qb][0] + lb_run[qb][1]) + (lb_run[qb][2] + lb_run[qb][3]));
     const int qi = qw0 + qb * 32 + l32;
     if (qi < N) {
-      const float inv = 1.f / lt;
+      const float inv = 1.f / lbt;
       bf16* O = a.o + base + (size_t)qi * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -444,7 +453,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_ref = -INFINITY, l_run = 0.f, mc = 0.f;
+  // running reference, float32 weight sum (LSE), rounded weight sum (output)
+  float m_ref = -INFINITY, l_run = 0.f, lb_run = 0.f, mc = 0.f;
   const float c = a.scale_log2;
 
   int k_lo, k_hi;
@@ -561,6 +571,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
           const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
           m_ref = m_new;
           l_run *= alpha;
+          lb_run *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -581,6 +592,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
           for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) P[u][e] = (bf16)S[8 * u + e];
+          lb_run = sum_bf16x16(P, lb_run);
         }
       };
 
@@ -625,7 +637,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
           }
           // keep the exp work in this stretch (it would otherwise sink to its
           // use in the P V step below)
-          asm volatile("" : "+v"(pop[P0][0]), "+v"(pop[P0][1]), "+v"(l_run));
+          asm volatile("" : "+v"(pop[P0][0]), "+v"(pop[P0][1]), "+v"(l_run), "+v"(lb_run));
           vread(kb, 0, vop[0]);
           vread(kb, 1, vop[1]);
           __builtin_amdgcn_sched_barrier(0);
@@ -664,8 +676,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
   }
 
   const float lt = pair_sum(l_run);
+  const float lbt = pair_sum(lb_run);
   if (qi < N) {
-    const float inv = 1.f / lt;
+    const float inv = 1.f / lbt;
     bf16* O = a.o + base + (size_t)qi * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)

@@ -13,8 +13,10 @@
 // State layout (workspace): per workgroup of 256 query rows and per wave of
 // 32 rows, the wave's accumulator registers as [DT*16/4][64 lanes] float4
 // (one coalesced 1 KiB access per group of four registers), then m and l as
-// [64 lanes] floats each. Lanes l and l+32 share query row l mod 32: m is
-// the same in both, l holds each half's partial sum.
+// [64 lanes] floats each, then the sum of the bf16-rounded weights (the
+// output's normalizer, as in the query-major kernel) as [64 lanes] floats.
+// Lanes l and l+32 share query row l mod 32: m is the same in both, the two
+// sums hold each half's part.
 #include "fa_common.h"
 #include "fa_kernels.h"
 #include "fa_tile_ops.h"
@@ -22,7 +24,7 @@
 namespace fa {
 
 template <int D>
-__device__ __forceinline__ size_t km_wave_floats() { return (size_t)64 * (D / 32 * 16 + 2); }
+__device__ __forceinline__ size_t km_wave_floats() { return (size_t)64 * (D / 32 * 16 + 3); }
 
 // state pointer of wave wv of workgroup w
 template <int D>
@@ -30,7 +32,7 @@ __device__ __forceinline__ float* km_state(float* ws, int w, int wv) {
   return ws + ((size_t)w * 8 + wv) * km_wave_floats<D>();
 }
 
-// m = -inf, l = 0, acc = 0 for every row
+// m = -inf, l = 0, rounded-weight sum = 0, acc = 0 for every row
 template <int D>
 __global__ __launch_bounds__(512) void km_init_kernel(float* ws, size_t n_wg) {
   constexpr int NACC = D / 32 * 16;
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(512) void km_init_kernel(float* ws, size_t n_wg) {
   for (int r = 0; r < NACC; ++r) st[(size_t)r * 64 + lane] = 0.f;
   st[(size_t)NACC * 64 + lane] = -INFINITY;
   st[(size_t)(NACC + 1) * 64 + lane] = 0.f;
+  st[(size_t)(NACC + 2) * 64 + lane] = 0.f;
 }
 
 // One key block j of BC keys: workgroup = 256 query rows (8 waves x 32),
@@ -96,6 +99,7 @@ __global__ __launch_bounds__(512, 2) void km_step_kernel(KmArgs a, int j) {
   }
   float m_ref = st[(size_t)NACC * 64 + lane];
   float l_run = st[(size_t)(NACC + 1) * 64 + lane];
+  float lb_run = st[(size_t)(NACC + 2) * 64 + lane];
   const float c = a.scale_log2;
 
   bf16x8 qop[KC];
@@ -148,6 +152,7 @@ __global__ __launch_bounds__(512, 2) void km_step_kernel(KmArgs a, int j) {
     const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
     m_ref = m_new;
     l_run *= alpha;
+    lb_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -161,11 +166,15 @@ __global__ __launch_bounds__(512, 2) void km_step_kernel(KmArgs a, int j) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
     l_run += sum16(sacc[kb]);
+    bf16x8 pops[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pops[u][e] = (bf16)sacc[kb][8 * u + e];
+    lb_run = sum_bf16x16(pops, lb_run);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      bf16x8 pop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pop[e] = (bf16)sacc[kb][8 * u + e];
+      const bf16x8 pop = pops[u];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
@@ -188,9 +197,10 @@ __global__ __launch_bounds__(512, 2) void km_step_kernel(KmArgs a, int j) {
   }
   st[(size_t)NACC * 64 + lane] = m_ref;
   st[(size_t)(NACC + 1) * 64 + lane] = l_run;
+  st[(size_t)(NACC + 2) * 64 + lane] = lb_run;
 }
 
-// O = acc / l and LSE = m scale + ln l from the final state
+// O = acc / (rounded-weight sum) and LSE = m scale + ln l from the final state
 template <int D>
 __global__ __launch_bounds__(512) void km_finalize_kernel(KmArgs a) {
   constexpr int DT = D / 32, NACC = DT * 16;
@@ -202,8 +212,9 @@ __global__ __launch_bounds__(512) void km_finalize_kernel(KmArgs a) {
   const float* st = km_state<D>(a.state, w, wv);
   const float m_ref = st[(size_t)NACC * 64 + lane];
   const float lt = pair_sum(st[(size_t)(NACC + 1) * 64 + lane]);
+  const float lbt = pair_sum(st[(size_t)(NACC + 2) * 64 + lane]);
   if (qi >= N) return;
-  const float inv = 1.f / lt;
+  const float inv = 1.f / lbt;
   bf16* O = a.o + (size_t)bh * N * D + (size_t)qi * D;
 #pragma unroll
   for (int g = 0; g < NACC / 4; ++g) {
@@ -243,7 +254,7 @@ static hipError_t km_mask(const KmArgs& a, int mask, hipStream_t stream) {
 
 size_t km_state_bytes(int BH, int N, int d) {
   const size_t n_wg = (size_t)BH * ((N + 255) / 256);
-  return n_wg * 8 * 64 * (size_t)(d / 32 * 16 + 2) * sizeof(float);
+  return n_wg * 8 * 64 * (size_t)(d / 32 * 16 + 3) * sizeof(float);
 }
 
 hipError_t launch_fwd_keymajor(const KmArgs& a0, int d, int bc, int mask, hipStream_t stream) {

@@ -55,12 +55,16 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters) {
   if (s == -1.2345e-30f) probe_sink = s;
 }
 
-// Grid-stride copy with 16-byte loads and stores (8 workgroups per compute
-// unit keep enough loads in flight; deeper unrolling measured slower).
+// Grid-stride copy with 16-byte non-temporal loads and stores, four
+// workgroups of 256 threads per compute unit: the fastest of the copy forms
+// measured on a 1 GiB buffer (6.16 TB/s, against 4.6-5.7 TB/s for plain
+// loads and stores at 2-16 workgroups per compute unit, unrolled loops or
+// contiguous per-workgroup chunks).
 __global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict__ src,
                                                          u32x4* __restrict__ dst, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace fa
@@ -124,7 +128,7 @@ extern "C" fa_status fa_probe_copy(const void* src, void* dst, size_t bytes, int
   if (cus < 1) return FA_ERR_LAUNCH;
   hipStream_t s = (hipStream_t)stream;
   const size_t n = bytes / 16;
-  const int blocks = 8 * cus;
+  const int blocks = 4 * cus;
   float ms = 0.f;
   const fa_status st = timed(s, [&] {
     for (int r = 0; r < reps; ++r) {

@@ -5,7 +5,9 @@
 //   1. S = scale Q K^T, float32, every (query, key) pair; masked pairs -inf;
 //   2. row softmax: m_i, l_i, LSE_i = m_i + ln l_i, and P = exp(S - m) / l
 //      written as bf16;
-//   3. O = P V.
+//   3. O = P V, divided by the row sum of the bf16-rounded P (1 up to that
+//      rounding), so that each output row is a convex combination of value
+//      rows with the weights the product actually used.
 // Workspace layout (fa_fwd_standard_workspace_bytes): S as [BH][N][lds]
 // float32 with lds = N rounded up to 4, then P as [BH][N][ldp] bf16 with
 // ldp = N rounded up to 8 (16-byte aligned rows).
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float psum = 0.f;  // this lane's part of the row sum of the rounded P
 
   dma(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -186,6 +189,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
         if (key < a.ldp) lo = *(const u32x2*)(P + key);
         if (key + 8 < a.ldp) hi = *(const u32x2*)(P + key + 8);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        psum = sum_bf16x8(pb, psum);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
+  const float inv = 1.f / pair_sum(psum);
   if (qi < N) {
     bf16* O = a.o + base + (size_t)qi * D;
 #pragma unroll
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (bf16)oacc[dt][4 * r4 + e];
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[dt][4 * r4 + e] * inv);
         *(bf16x4*)(O + dt * 32 + 8 * r4 + 4 * h) = y;
       }
   }

@@ -69,6 +69,45 @@ __device__ __forceinline__ float sum16(const f32x16& v) {
   return (a0 + a1) + (a2 + a3);
 }
 
+// Sum of the 16 bf16 weights of one 32-key block's P operand (two bf16x8),
+// added to acc with v_dot2c_f32_bf16 against (1, 1): the weights exactly as
+// the P V product uses them. Normalizing the output by this sum, rather than
+// by the float32 sum of the unrounded weights, makes each output row a convex
+// combination of value rows with the rounded weights; with the lazily
+// refreshed reference the dominant weight of a peaked row is a non-power of
+// two whose bf16 rounding would otherwise show as a relative error of up to
+// 2^-9 of the output.
+// (The pairs are taken with shufflevector: bit-casting the vector to four
+// dwords and each dword back to a bf16 pair has been compiled into four reads
+// of the first pair.)
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& p, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float sum_bf16x16(const bf16x8 (&p)[2], float acc) {
+  return sum_bf16x8(p[1], sum_bf16x8(p[0], acc));
+}
+// The same sum spread over four running accumulators (pair i of each bf16x8
+// into acc[i]), so that no two dependent dot products sit next to each other
+// in a wave's instruction stream: a single chain stalls the in-order issue,
+// and with it the next matrix instruction.
+__device__ __forceinline__ void sum_bf16x16_4(const bf16x8 (&p)[2], float (&acc)[4]) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    acc[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[u], p[u], 0, 1), one, acc[0], false);
+    acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[u], p[u], 2, 3), one, acc[1], false);
+    acc[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[u], p[u], 4, 5), one, acc[2], false);
+    acc[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[u], p[u], 6, 7), one, acc[3], false);
+  }
+}
+
 // Offset of accumulator register r within a 32-key block, for the lanes of
 // the lower half (the upper half adds 4): key = 8 (r / 4) + (r % 4).
 __device__ __forceinline__ constexpr int acc_key(int r) { return 8 * (r >> 2) + (r & 3); }

@@ -144,7 +144,8 @@ size_t fa_fwd_standard_workspace_bytes(int B, int H, int N, int d, fa_dtype dtyp
  * device memory, which is the traffic the notes' "Memory Hierarchy" section
  * counts. Same O and LSE contract as fa_fwd. Every (query, key) pair is
  * computed; masked pairs get score -inf and probability 0. P is normalized
- * before it is rounded to bf16 and multiplied by V.
+ * before it is rounded to bf16 and multiplied by V; each output row is then
+ * divided by its row sum of the rounded P (1 up to that rounding).
  *   q, k, v, o, lse : as fa_fwd; dtype must be FA_BF16 (d in {64, 128}).
  *   workspace       : device buffer of at least
  *                     fa_fwd_standard_workspace_bytes(...) bytes, owned by the
@@ -160,8 +161,9 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
 
 /*
  * Bytes of device workspace fa_fwd_keymajor needs: the running state of
- * every query row (float32 unnormalized output, maximum and denominator,
- * held by two lanes per row), B*H*ceil(N/256)*512*(d/2 + 2)*4 bytes.
+ * every query row (float32 unnormalized output, maximum, denominator and the
+ * sum of the bf16-rounded weights, held by two lanes per row),
+ * B*H*ceil(N/256)*512*(d/2 + 3)*4 bytes.
  * Returns 0 for an invalid problem or
  * a dtype other than FA_BF16.
  */

@@ -34,7 +34,8 @@ extern "C" {
 fa_status fa_probe_mfma_bf16(int iters, void* stream, double* tflops);
 
 /* HBM probe: a grid-stride copy of `bytes` bytes from src to dst with
- * 16-byte loads and stores, run `reps` times back to back. *gbs receives
+ * 16-byte non-temporal loads and stores (four workgroups of 256 threads per
+ * compute unit), run `reps` times back to back. *gbs receives
  * 2 * bytes * reps / elapsed seconds / 1e9 (bytes read plus bytes written).
  * src and dst are device pointers owned by the caller, 16-byte aligned and
  * non-overlapping; bytes is a positive multiple of 16. Errors: FA_ERR_NULL,

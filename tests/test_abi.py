@@ -118,9 +118,9 @@ def test_standard_workspace_and_errors(lib):
 
 
 def test_keymajor_workspace_and_errors(lib):
-    # two lanes per query row, 256-row workgroups: 512 * (d/2 + 2) floats each
-    assert lib.fa_fwd_keymajor_workspace_bytes(2, 3, 300, 128, 1) == 2 * 3 * 2 * 512 * 66 * 4
-    assert lib.fa_fwd_keymajor_workspace_bytes(1, 1, 256, 64, 1) == 512 * 34 * 4
+    # two lanes per query row, 256-row workgroups: 512 * (d/2 + 3) floats each
+    assert lib.fa_fwd_keymajor_workspace_bytes(2, 3, 300, 128, 1) == 2 * 3 * 2 * 512 * 67 * 4
+    assert lib.fa_fwd_keymajor_workspace_bytes(1, 1, 256, 64, 1) == 512 * 35 * 4
     assert lib.fa_fwd_keymajor_workspace_bytes(1, 1, 256, 64, 0) == 0
     ws = ctypes.c_void_p(0x4000000)
     def call(bc=64, d=64, dtype=1, ws=ws, wb=1 << 30):

@@ -114,3 +114,23 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU only" in r.stderr
+
+
+def test_cpu_baseline_keys(bench):
+    """The CPU-baseline leg on a tiny workload of the same recipe: dense and
+    tiled forward and dense backward timed per slice, the rate from the dense
+    pair, the thread count and the CPU model stated."""
+    from exact_tiled_attention_fwd_amd.synth import Workload, make_inputs
+    w = Workload("tiny_causal_bwd", 1, 3, 70, 16, "bf16", "causal", seed=1, backward=True)
+    inp = make_inputs(w)
+    r = bench.cpu_baseline(w, inp, True, target_s=0.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert r["cores"] == bench.omp_threads() >= 1
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+    for key in ("dense_fwd_s", "tiled_fwd_s", "dense_bwd_s"):
+        assert r[key] >= 0
+    assert r["sample"].startswith("1 of 3 (b,h) slices [1,1,70,16]")
+    ff = bench.fwd_flops(type(w)(**{**w.__dict__, "B": 1, "H": 1}))
+    fb = 2.5 * ff
+    assert abs(r["value"] - (ff + fb) / (r["dense_fwd_s"] + r["dense_bwd_s"]) / 1e12) <= \
+        1e-6 + 1e-2 * r["value"]

@@ -116,8 +116,10 @@ def test_deterministic():
 
 def test_full_size_backward_workload():
     """The causal backward workload [2, 16, 4096, 128] in the bench's launch
-    configuration: two whole (b, h) slices against the oracle, and the
-    gradient invariants on every slice."""
+    configuration: all 32 (b, h) slices against the oracle's dense backward,
+    relative Frobenius error of each gradient over the whole tensor (the worst
+    slice is reported too), and the gradient invariants."""
+    import time
     w = WORKLOADS["bf16_causal_bwd_b2h16_n4096_d128"]
     inp = make_inputs(w)
     q, k, v, do = (G.to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
@@ -126,13 +128,18 @@ def test_full_size_backward_workload():
     dq, dk, dv = attention_bwd(q, k, v, o, lse, do, w.scale, w.mask, w.window)
     torch.cuda.synchronize()
     B, H, N, d = w.shape
-    for bh in (0, B * H - 1):
-        sl = {n: inp[n].reshape(B * H, N, d)[bh] for n in ("q", "k", "v", "dout")}
-        ref = oracle.bwd_dense(sl["q"], sl["k"], sl["v"], sl["dout"], w.scale, w.mask, w.window)
-        for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
-            e = rel(g.reshape(B * H, N, d)[bh], ref[name])
-            print(f"slice {bh} {name}: rel {e:.3e}", flush=True)
-            assert e <= G.TOL_GRAD_REL, (bh, name, e)
+    t0 = time.perf_counter()
+    ref = oracle.bwd_dense(inp["q"], inp["k"], inp["v"], inp["dout"], w.scale, w.mask, w.window)
+    print(f"oracle dense backward over {B * H} slices: {time.perf_counter() - t0:.1f} s", flush=True)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        gn = G.f64(g).reshape(B * H, N, d)
+        rn = ref[name].reshape(B * H, N, d)
+        e = float(np.linalg.norm(gn - rn) / np.linalg.norm(rn))
+        per = np.linalg.norm((gn - rn).reshape(B * H, -1), axis=1) / np.linalg.norm(
+            rn.reshape(B * H, -1), axis=1)
+        print(f"{name}: rel {e:.3e} over the whole tensor; worst slice {int(per.argmax())}: "
+              f"{float(per.max()):.3e}", flush=True)
+        assert np.all(np.isfinite(gn)) and e <= G.TOL_GRAD_REL, (name, e)
     # invariants on every slice: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i
     dkf, dvf, dof = dk.double(), dv.double(), do.double()
     sk = dkf.sum(dim=2).norm() / dkf.norm()
@@ -147,7 +154,9 @@ def test_full_size_band_backward():
     configuration: sampled dQ rows and dK/dV rows (edges, tile boundaries and
     random rows of four heads) against the oracle's row-sampled backward,
     relative Frobenius error over the sampled rows; plus the invariants on
-    every slice."""
+    every slice. Sampled, not whole: the oracle's dense backward holds two
+    N x N matrices per head (2 x 2 GB here) and visits every pair, masked or
+    not, which at this length takes several host minutes per run."""
     w = WORKLOADS["bf16_local128_x8_bwd_b1h32_n16384_d128"]
     inp = make_inputs(w)
     q, k, v, do = (G.to_dev(inp[n]) for n in ("q", "k", "v", "dout"))

@@ -141,23 +141,21 @@ def test_errors_raise():
 
 @pytest.mark.parametrize("name", ["bf16_b4h16_n2048_d64", "bf16_causal_b2h16_n8192_d128",
                                   "bf16_local128_x8_b1h32_n16384_d128"])
-def test_full_size_sampled(name):
-    """Full workload sizes in the bench's launch configuration; sampled rows
-    against the dense oracle."""
+def test_full_size_whole_tensor(name):
+    """Full workload sizes in the bench's launch configuration: every row of
+    O and LSE against the dense oracle on the same seeded inputs (max-abs
+    2e-2 on O; 1e-4 + 1e-5 |LSE| on LSE)."""
+    import time
     w = WORKLOADS[name]
     inp = make_inputs(w)
     q, k, v = (G.to_dev(inp[n]) for n in ("q", "k", "v"))
     print(f"full-size {name}", flush=True)
     o, lse = attention_fwd(q, k, v, w.scale, w.mask, w.window)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.fwd_dense(inp["q"], inp["k"], inp["v"], w.scale, w.mask, w.window)
+    t_or = time.perf_counter() - t0
+    eo, el = G.check_fwd(o, lse, o_ref, lse_ref, BF16, name)
     B, H, N, d = w.shape
-    bh, rows, heads = G.sample_rows(B * H, N, 48, w.seed)
-    o_ref, lse_ref = G.oracle_rows(inp, w.scale, w.mask, w.window, bh, rows, heads)
-    o_g = o.reshape(B * H, N, d)[torch.as_tensor(bh), torch.as_tensor(rows)]
-    l_g = lse.reshape(B * H, N)[torch.as_tensor(bh), torch.as_tensor(rows)]
-    eo, el = G.check_fwd(o_g, l_g, o_ref, lse_ref, BF16, name)
-    print(f"{name}: max|dO|={eo:.3e} max|dLSE|={el:.3e} rows={len(rows)}", flush=True)
-    # properties at every row: finite, and |O| bounded by max |V| per column
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    vmax = v.float().abs().amax(dim=2, keepdim=True)
-    assert bool((o.float().abs() <= vmax * (1 + 2 ** -7) + 1e-6).all())
+    print(f"{name}: max|dO|={eo:.3e} max|dLSE|={el:.3e} over all {B * H * N} rows "
+          f"(oracle {t_or:.1f} s on the host)", flush=True)
