@@ -208,6 +208,11 @@ def main():
     ap.add_argument("--no-settle", action="store_true",
                     help="--std-sweep: skip the clock settle and the warm launches "
                          "(counter passes: only the flushed launches run)")
+    ap.add_argument("--std-bwd", action="store_true",
+                    help="--std-sweep: the backward pair instead (fused fa_bwd vs fa_bwd_standard, "
+                         "which reads the P stored by fa_fwd_standard)")
+    ap.add_argument("--summarize-std-bwd", default=None,
+                    help="HBM bytes of the fused vs standard backward from per-N counter CSVs in DIR")
     ap.add_argument("--summarize-std", default=None,
                     help="HBM bytes of fused vs standard from the per-N counter CSVs in DIR")
     ap.add_argument("--km-sweep", action="store_true",
@@ -233,6 +238,9 @@ def main():
         return
     if args.summarize_std:
         print(summarize_std(args.summarize_std, args.copy_mib))
+        return
+    if args.summarize_std_bwd:
+        print(summarize_std_bwd(args.summarize_std_bwd, args.copy_mib))
         return
     if args.summarize_km:
         print(summarize_km(args.summarize_km, args.copy_mib))
@@ -267,6 +275,9 @@ def main():
         return
     if args.gemm_ref:
         gemm_ref(torch, dev)
+        return
+    if args.std_sweep and args.std_bwd:
+        std_bwd_sweep(torch, fa, dev, args)
         return
     if args.std_sweep:
         std_sweep(torch, fa, dev, args)
@@ -658,6 +669,121 @@ def std_sweep(torch, fa, dev, args):
         print(f"| {N} | {ff * 1e3:.1f} | {fw * 1e3:.1f} | {sf * 1e3:.1f} | {sw * 1e3:.1f} | "
               f"{sf / ff:.2f} | {fb / 1e6:.1f} | {sb / 1e6:.1f} | {wsb / 1e9:.2f} |", flush=True)
         del q, k, v, o, lse, ws
+
+
+def std_bwd_bytes(N, B=1, H=16, d=64):
+    """Algorithmic HBM bytes of the two backwards at bf16 [B,H,N,d]. The
+    fused one reads Q, K, V, O, dO and the LSE and writes dQ, dK, dV
+    (bwd_bytes). The standard one reads Q, K, V, dO, writes dQ, dK, dV, and
+    moves per (query, key) pair: P read twice (dV and dS steps, 2 x 2 B), dP
+    written and read (2 x 4 B), dS written (2 B) and read twice (dQ and dK
+    steps, 2 x 2 B): 18 B."""
+    fused = 8 * B * H * N * d * 2 + B * H * N * 4
+    std = 7 * B * H * N * d * 2 + B * H * N * N * 18
+    return fused, std
+
+
+def std_bwd_sweep(torch, fa, dev, args):
+    """Time the fused backward (fa_bwd, recomputing P) and the standard one
+    (fa_bwd_standard, reading the P that fa_fwd_standard stored) on the
+    notes' setting (d = 64, no mask), B = 1, H = 16, N = 1024..16384 (or
+    --std-n); flushed and warm as in std_sweep."""
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(args.steps, 3)
+    print("| N | fused bwd flushed µs | fused bwd warm µs | standard bwd flushed µs | "
+          "standard bwd warm µs | standard / fused (flushed) | fused bytes (MB) | "
+          "standard bytes (MB) |")
+    print("|---|---|---|---|---|---|---|---|")
+    B, H, d = 1, 16, 64
+    for N in ([args.std_n] if args.std_n else STD_NS):
+        g = torch.Generator(device=dev).manual_seed(104729 + N)
+        q, k, v, do = (torch.randn(B, H, N, d, generator=g, device=dev).to(torch.bfloat16)
+                       for _ in range(4))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        wsf = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d, q.dtype), dtype=torch.uint8,
+                          device=dev)
+        fws = torch.empty(fa.fa_fwd_standard_workspace_bytes(B, H, N, d, q.dtype),
+                          dtype=torch.uint8, device=dev)
+        bws = torch.empty(fa.fa_bwd_standard_workspace_bytes(B, H, N, d, q.dtype),
+                          dtype=torch.uint8, device=dev)
+        fa.fa_fwd_standard(q, k, v, o, lse, fws, 0.125, "none", 0, stream)  # P for the standard bwd
+        fa.fa_fwd(q, k, v, o, lse, 0.125, "none", 0, stream)                # O, LSE for the fused
+        units = (lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, wsf, 0.125, "none", 0, stream),
+                 lambda: fa.fa_bwd_standard(q, k, v, do, fws, dq, dk, dv, bws, 0.125, stream))
+        res = [time_unit(torch, fn, stream, scratch, reps, not args.no_settle) for fn in units]
+        fb, sb = std_bwd_bytes(N, B, H, d)
+        (ff, fw), (sf, sw) = res
+        print(f"| {N} | {ff * 1e3:.1f} | {fw * 1e3:.1f} | {sf * 1e3:.1f} | {sw * 1e3:.1f} | "
+              f"{sf / ff:.2f} | {fb / 1e6:.1f} | {sb / 1e6:.1f} |", flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, wsf, fws, bws
+
+
+def _pmc_median_per_dispatch(path, counter):
+    """Median over dispatches of one counter, per kernel name (KiB), with the
+    number of dispatches."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {n: (statistics.median(v), len(v)) for n, v in out.items()}
+
+
+def summarize_std_bwd(d, copy_mib):
+    """Measured HBM bytes per call of the fused and the standard backward for
+    each N whose counter CSVs are in d (bfetch_N<n>_*, bwrite_N<n>_*, plus the
+    copy calibration), against std_bwd_bytes(). Each kernel counts with the
+    median over its dispatches (the one-off forwards that set up P, O and LSE
+    are dispatched once, the backwards several times), times its dispatches
+    per call (two for the transposed product: dV and dK)."""
+    one = lambda pat: sorted(glob.glob(os.path.join(d, pat)))[0]
+    cf = _pmc_per_dispatch(one("copy_fetch*_counter_collection.csv"), "FETCH_SIZE")
+    cw = _pmc_per_dispatch(one("copy_write*_counter_collection.csv"), "WRITE_SIZE")
+    ck = [n for n in cf if "copy" in n.lower()][0]
+    nbytes = copy_mib * (1 << 20)
+    f_fetch, f_write = nbytes / (cf[ck] * 1024.0), nbytes / (cw[ck] * 1024.0)
+    per_call = {"bwd_dq": 1, "bwd_dkdv": 1, "std_scores": 1, "std_xty": 2, "std_ds": 1,
+                "std_pv_kernel<64, false>": 1, "std_pv_kernel<128, false>": 1}
+    lines = ["| N | kernel | read MB per dispatch | written MB per dispatch | dispatches per call |",
+             "|---|---|---|---|---|"]
+    totals = []
+    for N in STD_NS:
+        fp = glob.glob(os.path.join(d, f"bfetch_N{N}_counter_collection.csv"))
+        wp = glob.glob(os.path.join(d, f"bwrite_N{N}_counter_collection.csv"))
+        if not fp or not wp:
+            continue
+        fe = _pmc_median_per_dispatch(fp[0], "FETCH_SIZE")
+        wr = _pmc_median_per_dispatch(wp[0], "WRITE_SIZE")
+        sums = {"fused": 0.0, "standard": 0.0}
+        for name in sorted(fe):
+            short = re.sub(r"\(.*", "", name).replace("void ", "")
+            key = next((k_ for k_ in per_call if k_ in short), None)
+            if key is None:
+                continue
+            unit = "fused" if key.startswith("bwd_") else "standard"
+            rb = fe[name][0] * 1024.0 * f_fetch
+            wb = wr.get(name, (0.0, 0))[0] * 1024.0 * f_write
+            sums[unit] += (rb + wb) * per_call[key]
+            lines.append(f"| {N} | `{short}` | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {per_call[key]} |")
+        totals.append((N, sums))
+    lines += ["", "| N | fused bwd MB (algorithmic) | standard bwd MB (algorithmic) | "
+              "standard / fused bytes |", "|---|---|---|---|"]
+    for N, sums in totals:
+        fb, sb = std_bwd_bytes(N)
+        lines.append(f"| {N} | {sums['fused'] / 1e6:.1f} ({fb / 1e6:.1f}) | "
+                     f"{sums['standard'] / 1e6:.1f} ({sb / 1e6:.1f}) | "
+                     f"{sums['standard'] / max(sums['fused'], 1.0):.1f} |")
+    lines += ["", f"Calibration: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f} "
+              f"(a {copy_mib} MiB copy through `{ck}`)."]
+    return "\n".join(lines)
 
 
 def summarize_std(d, copy_mib):

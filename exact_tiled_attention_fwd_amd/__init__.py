@@ -10,13 +10,15 @@ import math
 
 import torch
 
-from ._native import (FAError, fa_bwd, fa_bwd_tuned, fa_bwd_workspace_bytes, fa_fwd,
+from ._native import (FAError, fa_bwd, fa_bwd_noalloc, fa_bwd_standard,
+                      fa_bwd_standard_workspace_bytes, fa_bwd_tuned, fa_bwd_workspace_bytes, fa_fwd,
                       fa_fwd_keymajor, fa_fwd_keymajor_workspace_bytes, fa_fwd_standard,
                       fa_fwd_standard_workspace_bytes, fa_fwd_tuned, fa_probe_copy,
                       fa_probe_mfma_bf16, fa_status_string, load)
 
 __all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "load",
-           "fa_fwd_tuned", "fa_bwd_tuned",
+           "fa_fwd_tuned", "fa_bwd_tuned", "fa_bwd_noalloc", "fa_bwd_standard",
+           "fa_bwd_standard_workspace_bytes",
            "fa_fwd_standard", "fa_fwd_standard_workspace_bytes", "fa_fwd_keymajor",
            "fa_fwd_keymajor_workspace_bytes", "fa_probe_mfma_bf16",
            "fa_probe_copy", "attention_fwd", "attention_bwd"]

@@ -72,6 +72,11 @@ def load():
     lib.fa_fwd_standard.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                     i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_standard.restype = i
+    lib.fa_bwd_standard_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_standard_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_standard.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp,
+                                    ctypes.c_size_t, i, i, i, i, i, f, vp]
+    lib.fa_bwd_standard.restype = i
     lib.fa_fwd_keymajor_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_fwd_keymajor_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_keymajor.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -199,6 +204,33 @@ def fa_fwd_standard(q, k, v, o, lse, workspace, scale, mask=None, window=0, stre
                                 _stream(q, stream))
     if st != 0:
         raise FAError(st, "fa_fwd_standard")
+
+
+def fa_bwd_standard_workspace_bytes(B, H, N, d, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().fa_bwd_standard_workspace_bytes(int(B), int(H), int(N), int(d), code))
+
+
+def fa_bwd_standard(q, k, v, dout, fwd_workspace, dq, dk, dv, workspace, scale, stream=None):
+    """Call fa_bwd_standard: the unfused backward reading the P that
+    fa_fwd_standard left in `fwd_workspace`; `workspace` (uint8 GPU tensor of
+    at least fa_bwd_standard_workspace_bytes(...) bytes) holds dP and dS."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check("q", q)
+    for n, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(n, t, q, q.dtype, q.shape)
+    _check("fwd_workspace", fwd_workspace, q)
+    _check("workspace", workspace, q)
+    fb = fwd_workspace.numel() * fwd_workspace.element_size()
+    wb = workspace.numel() * workspace.element_size()
+    st = load().fa_bwd_standard(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                fwd_workspace.data_ptr(), fb, dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), workspace.data_ptr(), wb, B, H, N, d,
+                                _dtype_code(q), float(scale), _stream(q, stream))
+    if st != 0:
+        raise FAError(st, "fa_bwd_standard")
 
 
 def fa_fwd_keymajor_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -147,7 +147,7 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
       return FA_ERR_ALIAS;
   if (overlap(o, tb, lse, lb) || overlap(workspace, total, o, tb) || overlap(workspace, total, lse, lb))
     return FA_ERR_ALIAS;
-  fa::StdArgs a;
+  fa::StdArgs a = {};
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
   a.v = (const bf16*)v;
@@ -162,6 +162,62 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
   a.window = kernel_window(mask, window, N);
   a.scale = scale;
   const hipError_t e = fa::launch_std_bf16(a, d, (int)mask, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_standard_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
+  return fa_fwd_standard_workspace_bytes(B, H, N, d, dtype);
+}
+
+fa_status fa_bwd_standard(const void* q, const void* k, const void* v, const void* dout,
+                          const void* fwd_workspace, size_t fwd_workspace_bytes, void* dq,
+                          void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                          int H, int N, int d, fa_dtype dtype, float scale, void* stream) {
+  fa_status st = check_problem(B, H, N, d, dtype, scale, FA_MASK_NONE, 0);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if ((int64_t)B * H * N > kI32Max) return FA_ERR_SHAPE;  // one row workgroup per query row
+  size_t sb, total;
+  if (!std_layout(B, H, N, sb, total)) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!fwd_workspace || fwd_workspace_bytes < total || !workspace || workspace_bytes < total)
+    return FA_ERR_WORKSPACE;
+  const void* all[] = {q, k, v, dout, fwd_workspace, dq, dk, dv, workspace};
+  for (const void* p : all)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const void* ins[] = {q, k, v, dout};
+  void* outs[] = {dq, dk, dv};
+  for (void* o : outs) {
+    for (const void* in : ins)
+      if (overlap(o, tb, in, tb)) return FA_ERR_ALIAS;
+    if (overlap(o, tb, fwd_workspace, total) || overlap(o, tb, workspace, total)) return FA_ERR_ALIAS;
+  }
+  if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
+    return FA_ERR_ALIAS;
+  for (const void* in : ins)
+    if (overlap(workspace, total, in, tb)) return FA_ERR_ALIAS;
+  if (overlap(workspace, total, fwd_workspace, total)) return FA_ERR_ALIAS;
+  fa::StdArgs a;
+  a.q = (const bf16*)q;
+  a.k = (const bf16*)k;
+  a.v = (const bf16*)v;
+  a.dout = (const bf16*)dout;
+  a.o = nullptr;
+  a.lse = nullptr;
+  a.p = (bf16*)((char*)fwd_workspace + sb);  // the forward's P, read only
+  a.s = (float*)workspace;                   // dP
+  a.ds = (bf16*)((char*)workspace + sb);     // dS
+  a.dq = (bf16*)dq;
+  a.dk = (bf16*)dk;
+  a.dv = (bf16*)dv;
+  a.BH = B * H;
+  a.N = N;
+  a.lds = (N + 3) & ~3;
+  a.ldp = (N + 7) & ~7;
+  a.window = 0;
+  a.scale = scale;
+  const hipError_t e = fa::launch_std_bwd_bf16(a, d, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -49,6 +49,12 @@ struct StdArgs {
   int ldp;     // N rounded up to 8
   int window;
   float scale;  // signed scale as given
+  // standard backward only
+  const bf16* dout;   // dO
+  bf16* ds;           // workspace: [BH][N][ldp] bf16 dS (the P region's layout)
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
 };
 
 // Key-major forward: per key block one launch updating a running state.
@@ -74,6 +80,9 @@ hipError_t launch_fwd_keymajor(const KmArgs& a, int d, int bc, int mask, hipStre
 // cfg selects a tile configuration (0 = default); tuning only.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream_t stream);
 hipError_t launch_std_bf16(const StdArgs& a, int d, int mask, hipStream_t stream);
+// standard backward: dP = dO V^T into a.s, dV = P^T dO, D and dS into a.ds,
+// dQ = scale dS K, dK = scale dS^T Q (P read from a.p)
+hipError_t launch_std_bwd_bf16(const StdArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdF32Args& a, int mask, hipStream_t stream);
 
 }  // namespace fa

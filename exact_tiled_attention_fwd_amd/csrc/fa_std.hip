@@ -11,6 +11,16 @@
 // Workspace layout (fa_fwd_standard_workspace_bytes): S as [BH][N][lds]
 // float32 with lds = N rounded up to 4, then P as [BH][N][ldp] bf16 with
 // ldp = N rounded up to 8 (16-byte aligned rows).
+//
+// The standard backward (the notes' "Backward Pass: Recomputation" contrasts
+// it with the recomputing one) reads the stored P instead of recomputing it,
+// and makes each N x N intermediate a round trip through device memory too:
+//   4. dP = dO V^T, float32, into a workspace of the forward's layout (S region);
+//   5. dV = P^T dO;
+//   6. D_i = sum_j P_ij dP_ij and dS = P (dP - D), bf16 (P region of that workspace);
+//   7. dQ = scale dS K (the P V kernel without normalization);
+//   8. dK = scale dS^T Q.
+// The chain rule behind 5-8 is the one the recomputing backward uses.
 #include "fa_common.h"
 #include "fa_kernels.h"
 #include "fa_tile_ops.h"
@@ -135,8 +145,13 @@ __global__ __launch_bounds__(256) void std_softmax_kernel(StdArgs a) {
 // operand of O^T = V^T P^T; P rows come from memory as the B operand, each
 // lane taking the 8 keys of one query that match the transposed V read
 // (keys 16u + 4h + {0..3} and 16u + 8 + 4h + {0..3} of step u).
-template <int D>
-__global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
+// NORM: divide each row by its sum of the rounded weights (the forward's
+// O = P V); otherwise multiply by out_scale (the backward's dQ = scale dS K,
+// with p = dS, v = K, o = dQ).
+template <int D, bool NORM>
+__global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a, const bf16* __restrict__ pm,
+                                                     const bf16* __restrict__ vm,
+                                                     bf16* __restrict__ om, float out_scale) {
   constexpr int BC = 64, DT = D / 32, KB = BC / 32, ROWB = D * 2, TILEB = BC * ROWB, CPR = D / 8;
   constexpr int CPT = BC * CPR / 512;
   __shared__ __attribute__((aligned(16))) char sV[2 * TILEB];
@@ -146,7 +161,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
   const int bh = blockIdx.x / n_qt, qt = blockIdx.x % n_qt;
   const size_t base = (size_t)bh * N * D;
   const int qi = qt * 256 + wv * 32 + l32;
-  const bf16* P = a.p + ((size_t)bh * N + (qi < N ? qi : N - 1)) * a.ldp;
+  const bf16* P = pm + ((size_t)bh * N + (qi < N ? qi : N - 1)) * a.ldp;
   const int n_tiles = (N + BC - 1) / BC;
 
   auto dma = [&](int t, int buf) {
@@ -157,7 +172,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
       const int row = p / CPR;
       int gr = t * BC + row;
       gr = gr < N ? gr : N - 1;  // P is 0 for keys past N
-      lds_dma16(a.v + base + (size_t)gr * D + ((p % CPR) ^ swz_v16<D>(row)) * 8,
+      lds_dma16(vm + base + (size_t)gr * D + ((p % CPR) ^ swz_v16<D>(row)) * 8,
                 lds_addr(sV + buf * TILEB + slot * 16));
     }
   };
@@ -189,7 +204,7 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
         if (key < a.ldp) lo = *(const u32x2*)(P + key);
         if (key + 8 < a.ldp) hi = *(const u32x2*)(P + key + 8);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        psum = sum_bf16x8(pb, psum);
+        if constexpr (NORM) psum = sum_bf16x8(pb, psum);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
@@ -204,9 +219,9 @@ __global__ __launch_bounds__(512) void std_pv_kernel(StdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
-  const float inv = 1.f / pair_sum(psum);
+  const float inv = NORM ? 1.f / pair_sum(psum) : out_scale;
   if (qi < N) {
-    bf16* O = a.o + base + (size_t)qi * D;
+    bf16* O = om + base + (size_t)qi * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -229,8 +244,145 @@ static hipError_t launch_std_mask(const StdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(std_softmax_kernel, dim3((unsigned)((long)a.BH * a.N)), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((std_pv_kernel<D>), dim3((unsigned)(n_qt * a.BH)), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((std_pv_kernel<D, true>), dim3((unsigned)(n_qt * a.BH)), dim3(512), 0, stream, a,
+                     (const bf16*)a.p, a.v, a.o, 1.f);
   return hipGetLastError();
+}
+
+// ---- standard backward, step 6: one workgroup per row: D_i = sum_j P_ij
+// dP_ij (float32, reduced over the workgroup), then dS_ij = P_ij (dP_ij - D_i)
+// as bf16 (rows padded to ldp with zeros).
+__global__ __launch_bounds__(256) void std_ds_kernel(StdArgs a) {
+  __shared__ float sd[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t row = blockIdx.x;  // bh * N + i
+  const int N = a.N;
+  const float* dp = a.s + row * a.lds;
+  const bf16* p = a.p + row * a.ldp;
+  float acc = 0.f;
+  for (int j = tid; j < N; j += 256) acc = __builtin_fmaf((float)p[j], dp[j], acc);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) sd[wv] = acc;
+  __syncthreads();
+  const float Di = (sd[0] + sd[1]) + (sd[2] + sd[3]);
+  bf16* ds = a.ds + row * a.ldp;
+  for (int j = tid; j < a.ldp; j += 256)
+    ds[j] = (bf16)(j < N ? (float)p[j] * (dp[j] - Di) : 0.f);
+}
+
+// ---- standard backward, steps 5 and 8: out = alpha X^T Y, i.e.
+// out[j][c] = alpha sum_i X[i][j] Y[i][c], with X an N x N bf16 matrix of row
+// stride ldp (P or dS) and Y an N x D bf16 matrix (dO or Q). Workgroup: 256
+// output rows j (8 waves x 32); i runs over tiles of 32 rows staged in LDS
+// (X: 32 x 256 columns, Y: 32 x D), both read transposed with
+// ds_read_b64_tr_b16 so that i is the contraction index of
+// out^T = Y^T X on v_mfma_f32_32x32x16_bf16: lane (j, half h) gets the rows
+// 16u + 4h + {0..3} and 16u + 8 + 4h + {0..3} of its column from both tiles,
+// the same row order, so the products pair up.
+template <int D>
+__global__ __launch_bounds__(512) void std_xty_kernel(StdArgs a, const bf16* __restrict__ X,
+                                                      const bf16* __restrict__ Y,
+                                                      bf16* __restrict__ out, float alpha) {
+  constexpr int DT = D / 32, ROWY = D * 2, ROWX = 256 * 2, TI = 32;
+  __shared__ __attribute__((aligned(16))) char sY[TI * ROWY];
+  __shared__ __attribute__((aligned(16))) char sX[TI * ROWX];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5;
+  const int N = a.N;
+  const int n_jt = (N + 255) / 256;
+  const int bh = blockIdx.x / n_jt, jt = blockIdx.x % n_jt;
+  const int j0 = jt * 256;
+  const bf16* Xh = X + (size_t)bh * N * a.ldp;
+  const bf16* Yh = Y + (size_t)bh * N * D;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  for (int i0 = 0; i0 < N; i0 += TI) {
+    // stage: Y rows i0.. (16-byte chunks, zero past N), X rows i0.., columns
+    // j0..j0+255 (zero past the padded row length ldp)
+    for (int c = tid; c < TI * D / 8; c += 512) {
+      const int r = c / (D / 8), cc = c % (D / 8);
+      u32x4 y = {0u, 0u, 0u, 0u};
+      if (i0 + r < N) y = *(const u32x4*)(Yh + (size_t)(i0 + r) * D + cc * 8);
+      *(u32x4*)(sY + r * ROWY + cc * 16) = y;
+    }
+    for (int c = tid; c < TI * 32; c += 512) {
+      const int r = c / 32, cc = c % 32;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      const int col = j0 + cc * 8;
+      if (i0 + r < N && col < a.ldp) x = *(const u32x4*)(Xh + (size_t)(i0 + r) * a.ldp + col);
+      *(u32x4*)(sX + r * ROWX + cc * 16) = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rlo = 16 * u + tr_row, rhi = rlo + 8;
+      const int xc = (wv * 8 + tr_ch8) * 8;  // this wave's 32 columns, in bytes
+      const i16x4 xlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sX + rlo * ROWX + xc));
+      const i16x4 xhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sX + rhi * ROWX + xc));
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(xlo, xhi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int yc = (dt * 8 + tr_ch8) * 8;
+        const i16x4 ylo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sY + rlo * ROWY + yc));
+        const i16x4 yhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sY + rhi * ROWY + yc));
+        const bf16x8 ya = __builtin_bit_cast(bf16x8, __builtin_shufflevector(ylo, yhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ya, xb, acc[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  const int j = j0 + wv * 32 + (lane & 31);
+  if (j < N) {
+    bf16* o = out + ((size_t)bh * N + j) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)(acc[dt][4 * r4 + e] * alpha);
+        *(bf16x4*)(o + dt * 32 + 8 * r4 + 4 * h) = y;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_std_bwd_d(const StdArgs& a0, hipStream_t stream) {
+  const long n_kt = (a0.N + 127) / 128, n_qt = (a0.N + 255) / 256;
+  hipError_t e;
+  // 4. dP = dO V^T: the score kernel with dO for Q, V for K, scale 1, no mask
+  StdArgs a = a0;
+  a.q = a0.dout;
+  a.k = a0.v;
+  a.scale = 1.f;
+  hipLaunchKernelGGL((std_scores_kernel<D, MASK_NONE>), dim3((unsigned)(n_kt * n_qt * a.BH)), dim3(512), 0,
+                     stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 5. dV = P^T dO
+  hipLaunchKernelGGL((std_xty_kernel<D>), dim3((unsigned)(n_qt * a0.BH)), dim3(512), 0, stream, a0,
+                     (const bf16*)a0.p, a0.dout, a0.dv, 1.f);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 6. D and dS
+  hipLaunchKernelGGL(std_ds_kernel, dim3((unsigned)((long)a0.BH * a0.N)), dim3(256), 0, stream, a0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 7. dQ = scale dS K
+  hipLaunchKernelGGL((std_pv_kernel<D, false>), dim3((unsigned)(n_qt * a0.BH)), dim3(512), 0, stream, a0,
+                     (const bf16*)a0.ds, a0.k, a0.dq, a0.scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 8. dK = scale dS^T Q
+  hipLaunchKernelGGL((std_xty_kernel<D>), dim3((unsigned)(n_qt * a0.BH)), dim3(512), 0, stream, a0,
+                     (const bf16*)a0.ds, a0.q, a0.dk, a0.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_std_bwd_bf16(const StdArgs& a, int d, hipStream_t stream) {
+  return d == 128 ? launch_std_bwd_d<128>(a, stream) : launch_std_bwd_d<64>(a, stream);
 }
 
 hipError_t launch_std_bf16(const StdArgs& a, int d, int mask, hipStream_t stream) {

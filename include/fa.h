@@ -160,6 +160,37 @@ fa_status fa_fwd_standard(const void* q, const void* k, const void* v, void* o, 
                           float scale, fa_mask mask, int window, void* stream);
 
 /*
+ * Bytes of device workspace fa_bwd_standard needs for its own intermediates:
+ * dP (float32) and dS (bf16), in the layout of fa_fwd_standard's workspace,
+ * so the same number of bytes. Returns 0 as fa_fwd_standard_workspace_bytes.
+ */
+size_t fa_bwd_standard_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Standard (unfused) backward, the baseline fa_bwd is measured against: it
+ * reads the probabilities P that fa_fwd_standard stored instead of
+ * recomputing them (the contrast the notes' "Backward Pass: Recomputation"
+ * draws), and every N x N intermediate makes a round trip through device
+ * memory: dP = dO V^T (float32), dV = P^T dO, D_i = sum_j P_ij dP_ij and
+ * dS = P (dP - D) (bf16), dQ = scale dS K, dK = scale dS^T Q. Same gradients
+ * as fa_bwd (up to rounding); masked pairs need no mask here, as their P is 0.
+ *   q, k, v, dout  : inputs [B][H][N][d], bf16 (d in {64, 128}).
+ *   fwd_workspace  : the workspace of a fa_fwd_standard call with the same
+ *                    q, k, v, scale and mask, at least
+ *                    fa_fwd_standard_workspace_bytes(...) bytes; read only.
+ *   dq, dk, dv     : outputs [B][H][N][d] bf16.
+ *   workspace      : at least fa_bwd_standard_workspace_bytes(...) bytes,
+ *                    owned by the caller, 16-byte aligned, overlapping no
+ *                    other buffer; contents ignored and undefined on return.
+ * Errors: as fa_bwd; FA_ERR_DTYPE for FA_F32; FA_ERR_WORKSPACE when either
+ * workspace is missing or too small; FA_ERR_SHAPE when B*H*N > 2^31-1.
+ */
+fa_status fa_bwd_standard(const void* q, const void* k, const void* v, const void* dout,
+                          const void* fwd_workspace, size_t fwd_workspace_bytes,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          int B, int H, int N, int d, fa_dtype dtype, float scale, void* stream);
+
+/*
  * Bytes of device workspace fa_fwd_keymajor needs: the running state of
  * every query row (float32 unnormalized output, maximum, denominator and the
  * sum of the bf16-rounded weights, held by two lanes per row),

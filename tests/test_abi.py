@@ -157,3 +157,22 @@ def test_window_marshalling():
     assert _native._window(2 ** 31 - 1) == 2 ** 31 - 1
     assert _native._window(2 ** 31) == 2 ** 31 - 1 and _native._window(2 ** 63) == 2 ** 31 - 1
     assert _native._window(-1) == -1 and _native._window(-(2 ** 32) + 5) == -1
+
+
+def test_standard_backward_workspace_and_errors(lib):
+    assert lib.fa_bwd_standard_workspace_bytes(1, 2, 300, 128, 1) == \
+        lib.fa_fwd_standard_workspace_bytes(1, 2, 300, 128, 1)
+    assert lib.fa_bwd_standard_workspace_bytes(1, 2, 300, 128, 0) == 0
+    need = lib.fa_bwd_standard_workspace_bytes(1, 1, 8, 64, 1)
+    f, w = ctypes.c_void_p(0x4000000), ctypes.c_void_p(0x8000000)
+    outs = [ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000), ctypes.c_void_p(0x400000)]
+    def call(fws=f, fb=need, ws=w, wb=need, dtype=1, d=64, q=FAKE, scale=0.125):
+        return lib.fa_bwd_standard(q, FAKE, FAKE, FAKE, fws, fb, *outs, ws, wb, 1, 1, 8, d, dtype,
+                                   scale, None)
+    assert call(q=None) == 1
+    assert call(dtype=0) == 3 and call(d=96) == 4
+    assert call(fws=None) == 8 and call(fb=need - 1) == 8
+    assert call(ws=None) == 8 and call(wb=16) == 8
+    assert call(ws=ctypes.c_void_p(0x8000008)) == 7
+    assert call(ws=f) == 10                         # the two workspaces overlap
+    assert call(scale=float("nan")) == 6
