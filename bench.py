@@ -119,7 +119,8 @@ def _pmc_per_dispatch(path, counter):
 
 
 def summarize_pmc(d, copy_mib, workload):
-    """Markdown summary of the FETCH_SIZE / WRITE_SIZE passes in directory d:
+    """Markdown summary of the FETCH_SIZE / WRITE_SIZE passes in directory d
+    (bytes between L2 and the memory fabric; the MALL may serve part of them):
     bench run on `workload` (fetch_*, write_*) and the copy calibration
     (copy_fetch_*, copy_write_*). Counter readings are scaled so that the
     plain copy of copy_mib MiB reads and writes exactly that many bytes."""
@@ -157,7 +158,8 @@ def summarize_pmc(d, copy_mib, workload):
               f"WRITE_SIZE by {f_write:.3f}.", ""]
     for u, x in units.items():
         lines.append(f"- `{u}` per call: {x['read_bytes'] / 1e6:.1f} MB read + "
-                     f"{x['write_bytes'] / 1e6:.1f} MB written from/to HBM")
+                     f"{x['write_bytes'] / 1e6:.1f} MB written between L2 and the memory fabric "
+                     f"(HBM or the MALL)")
     lines += ["", f"<!-- {TRAFFIC_TAG} {json.dumps(meta)} -->"]
     return "\n".join(lines)
 
@@ -373,6 +375,10 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                 "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": traffic, "traffic_unit": "bytes per call", "traffic_source": traffic_src,
+                "traffic_counts": "bytes between L2 and the memory fabric (FETCH_SIZE + WRITE_SIZE, "
+                                  "scaled by a device copy of known size); the 256 MB MALL behind "
+                                  "the fabric may serve part of them, so they bound HBM bytes "
+                                  "from above",
                 "algorithmic_bytes_per_launch": by_dom, "kernel": dom,
                 "arithmetic_intensity": round(fl_dom / by_dom, 1),
                 "peak_measured": round(pk_meas, 1),
