@@ -15,7 +15,7 @@ namespace {
 
 // Kernel choice of the forward: 0 is the measured default; other values
 // select the alternative shapes kept for timing comparisons (fa_tuning.h).
-constexpr int kFwdCfgMax = 8;
+constexpr int kFwdCfgMax = 9;
 
 void set_scale(const ScaleFold& f, fa::FwdArgs& a) {
   a.scale_abs = f.scale_abs;

@@ -36,6 +36,8 @@
 //    exp2 units, so most tiles skip the rescale of the accumulator (p then
 //    stays below 2^RESCALE_LOG2, harmless in float32 and bf16). Numerator
 //    and denominator share the reference, so the result is unchanged.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 #include "fa_tile_ops.h"
@@ -693,6 +695,333 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
   }
 }
 
+// Ping-pong variant of the tile kernel. The two waves that share a SIMD
+// (w and w + 4 of the eight) run the same per-tile program,
+//   M(t): O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t
+//         (matrix core and LDS reads only);
+//   X(t): mask, row maximum, reference check and exp of tile t
+//         (vector ALU only),
+// with a workgroup barrier after each phase, but the second wave of each
+// SIMD starts one phase late. From then on every SIMD holds one wave in an
+// M phase and one in an X phase, so the matrix core and the vector ALU work
+// at the same time instead of taking turns. P of tile t waits in registers
+// (bf16) until the next M phase.
+// LDS: K of tile t is read in the M(t) phases of both waves, V of tile t in
+// their M(t+1) phases, so the loads of K(t+1) and V(t) share one window of
+// two phases: issued at the start of the first wave's M(t) phase (the second
+// wave issues its part at the same moment, in its X(t-1) phase), waited for
+// before the barrier that ends that window.
+template <int D, int QB, int BC, int MASK>
+__global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int NT = NW * 64;
+  constexpr int QW = QB * 32;
+  constexpr int BR = NW * QW;
+  constexpr int KC = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KB = BC / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BC * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BC * CPR / NT;
+  static_assert((BC * CPR) % NT == 0 && BC <= 128, "tile chunks must divide evenly");
+  static_assert(BC % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
+
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];  // K[2], V[2]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int N = a.N;
+
+  int bh, qt;
+  wg_tile(blockIdx.x, a.BH, a.n_qtiles, bh, qt);
+  if (MASK == MASK_CAUSAL) qt = a.n_qtiles - 1 - qt;
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const bf16* __restrict__ Q = a.q + base;
+  const bf16* __restrict__ K = a.k + base;
+  const bf16* __restrict__ V = a.v + base;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wv * QW;
+
+  bf16x8 qop[QB][KC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row < N) x = *(const u32x4*)(Q + (size_t)row * D + kc * 16 + h * 8);
+      x = (x & a.q_and) ^ a.q_xor;
+      qop[qb][kc] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 oacc[QB][DT];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
+  float m_ref[QB], l_run[QB], lb_run[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lb_run[qb][i] = 0.f;
+  }
+  const float c = a.scale_log2;
+
+  int k_lo, k_hi;
+  key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
+  const int t_begin = k_lo / BC;
+  const int t_end = (k_hi + BC - 1) / BC;
+  int wk_lo, wk_hi;
+  key_range<MASK>(qw0, qw0 + QW, N, a.window, wk_lo, wk_hi);
+  const bool wave_live = qw0 < N;
+
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const bool lead = wvu < NW / 2;
+  // The first wave of each SIMD issues all tile loads (CPL chunks each), at
+  // the start of its M phases; the second never touches global memory in
+  // the loop. Offsets are recomputed at each load from an opaque copy of the
+  // lane index, so that no per-load address stays live across the loop.
+  constexpr int CPL = 2 * CPT;
+  auto dma = [&](auto is_v, const bf16* G, int t, char* dst) {
+    constexpr bool ISV = decltype(is_v)::value;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int k0 = t * BC;
+    const char* g = (const char*)G + (size_t)k0 * ROWB;
+    const int rmax = N - 1 - k0;  // rows past N are clamped (their keys are masked)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int slot = (wvu * CPL + j) * 64;
+      const int p = slot + ln;
+      const int row = p / CPR;
+      const int gr = min(row, rmax);
+      const unsigned off = gr * ROWB + (((p % CPR) ^ (ISV ? swz_v16<D>(row) : swz_k16<D>(row))) << 4);
+      lds_dma16_s(g, off, lds_addr(dst + slot * 16));
+    }
+  };
+  char* const sK0 = smem;
+  char* const sK1 = smem + TILEB;
+  char* const sV0 = smem + 2 * TILEB;
+  char* const sV1 = smem + 3 * TILEB;
+  // loads of window j (tile t = t_begin + j): K(t + 1) into K buffer
+  // (j + 1) & 1 and V(t) into V buffer j & 1
+  auto window_dma = [&](int t, auto jpar) {
+    constexpr int JP = decltype(jpar)::value;
+    if (t + 1 < t_end) dma(std::false_type{}, K, t + 1, JP ? sK0 : sK1);
+    if (t < t_end) dma(std::true_type{}, V, t, JP ? sV1 : sV0);
+  };
+
+  const int g16 = lane >> 4;
+  const int s16 = lane & 15;
+  const int tr_row = 4 * h + (s16 >> 2);
+  const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
+
+  if (lead && t_begin < t_end) {
+    dma(std::false_type{}, K, t_begin, sK0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  __syncthreads();
+  if (!lead) __syncthreads();  // the second wave of each SIMD runs one phase late
+
+  f32x16 sacc[QB][KB];
+  bf16x8 pop[QB][KB][2];
+  bool have_p = false;  // pop holds P of the previous tile
+
+  // one (M, X) pair of tile t = t_begin + j; JP = j & 1 (buffer parity)
+  auto step = [&](int t, auto jpar) {
+    constexpr int JP = decltype(jpar)::value;
+    const char* sK = JP ? sK1 : sK0;       // K(t)
+    const char* sV = JP ? sV0 : sV1;       // V(t - 1)
+    const int k0 = t * BC;
+    const bool live = t < t_end && wave_live && k0 < wk_hi && k0 + BC > wk_lo;
+
+    // ---------------- M phase
+    if (lead) window_dma(t, jpar);
+    if (have_p) {
+      bf16x8 vop[2][DT];
+      auto vread = [&](int kb, int u) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rlo = kb * 32 + 16 * u + tr_row, rhi = rlo + 8;
+          const int clo = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rlo) << 1)) * 8;
+          const int chi = ((dt * 8 + tr_ch8) ^ (swz_v16<D>(rhi) << 1)) * 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rlo * ROWB + clo));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(sV + rhi * ROWB + chi));
+          vop[u][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          vread(kb, u);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[qb][kb][u], oacc[qb][dt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (live) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+      bf16x8 kop[2][KB];
+      auto kread = [&](int kc, int slot) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int row = kb * 32 + l32;
+          kop[slot][kb] = *(const bf16x8*)(sK + row * ROWB + (((2 * kc + h) ^ swz_k16<D>(row)) << 4));
+        }
+      };
+      kread(0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (kc + 1 < KC) kread(kc + 1, (kc + 1) & 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc & 1][kb], qop[qb][kc], sacc[qb][kb], 0, 0, 0);
+        if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KB * QB, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+
+    // ---------------- X phase
+    have_p = live;
+    if (live) {
+      if ((k0 + BC > N) || !tile_full<MASK>(qw0, qw0 + QW, k0, k0 + BC, a.window)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qi = qw0 + qb * 32 + l32;
+          const int q_hi_key = MASK == MASK_CAUSAL ? min(qi, N - 1)
+                               : MASK == MASK_LOCAL ? min(qi + a.window, N - 1) : N - 1;
+          const int hoff = 4 * h;
+          const int hi_rel = q_hi_key - k0 - hoff;
+          const int lo_rel = (MASK == MASK_LOCAL ? qi - a.window : 0) - k0 - hoff;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kr = kb * 32 + acc_key(r);
+              const bool ok =
+                  (MASK == MASK_LOCAL) ? (kr <= hi_rel && kr >= lo_rel) : (kr <= hi_rel);
+              sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
+            }
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = max16(sacc[qb][0]);
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, max16(sacc[qb][kb]));
+        mx = pair_max(mx);
+        if (__builtin_amdgcn_ballot_w64((mx - m_ref[qb]) * c > RESCALE_LOG2)) {
+          const float m_new = fmaxf(m_ref[qb], mx);
+          const float alpha =
+              m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref[qb] - m_new) * c);
+          m_ref[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lb_run[qb][i] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+        }
+        const float mc = (m_ref[qb] == -INFINITY ? 0.f : m_ref[qb]) * c;
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[qb][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][r], c, -mc));
+          ls += sum16(sacc[qb][kb]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pop[qb][kb][u][e] = (bf16)sacc[qb][kb][8 * u + e];
+          sum_bf16x16_4(pop[qb][kb], lb_run[qb]);
+        }
+        l_run[qb] += ls;
+      }
+    } else {
+      // (nothing reads P after a skipped tile; a defined value here ends the
+      // previous P's live range at the last P V instead of carrying it on)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) pop[qb][kb][u] = bf16x8{};
+    }
+    if (lead) __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  // t runs one past the last tile: its M phase holds the last P V
+  int t = t_begin;
+  for (; t + 1 <= t_end; t += 2) {
+    step(t, ic<0>{});
+    step(t + 1, ic<1>{});
+  }
+  if (t <= t_end) step(t, ic<0>{});
+  if (lead) __syncthreads();
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = pair_sum(l_run[qb]);
+    const float lbt = pair_sum((lb_run[qb][0] + lb_run[qb][1]) + (lb_run[qb][2] + lb_run[qb][3]));
+    const int qi = qw0 + qb * 32 + l32;
+    if (qi < N) {
+      const float inv = 1.f / lbt;
+      bf16* O = a.o + base + (size_t)qi * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[qb][dt][4 * r4 + e] * inv);
+          *(bf16x4*)(O + dt * 32 + 8 * r4 + 4 * h) = y;
+        }
+      if (h == 0) a.lse[(size_t)bh * N + qi] = m_ref[qb] * a.scale_abs + logf(lt);
+    }
+  }
+}
+
+template <int D, int QB, int BC>
+static hipError_t launch_fwd_bf16_pp(const FwdArgs& a0, int mask, hipStream_t stream) {
+  FwdArgs a = a0;
+  constexpr int BR = 8 * QB * 32;
+  a.n_qtiles = (a.N + BR - 1) / BR;
+  dim3 grid((unsigned)(a.n_qtiles * a.BH)), block(512);
+  switch (mask) {
+    case MASK_CAUSAL: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, QB, BC, MASK_CAUSAL>), grid, block, 0, stream, a); break;
+    case MASK_LOCAL: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, QB, BC, MASK_LOCAL>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, QB, BC, MASK_NONE>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int BC>
 static hipError_t launch_fwd_bf16_xb(const FwdArgs& a0, int mask, hipStream_t stream) {
   FwdArgs a = a0;
@@ -739,6 +1068,15 @@ static hipError_t launch_fwd_bf16_cfg(const FwdArgs& a0, int mask, hipStream_t s
 // memory latency: 163 -> 156 and 158.6 -> 154.3 us on two cards. At d = 64
 // the band takes one query block per wave and 32-key tiles (100 VGPRs, five
 // waves per SIMD): 112 -> 76 us on [1, 32, 16384, 64] with radius 128.
+// cfg 9 is the ping-pong schedule (fwd_bf16_pp_kernel). It passes the same
+// parity tests but is slower at d = 128 (534.6 vs 498.4 us on causal
+// [2, 16, 8192, 128]) and even at d = 64 (77.5 vs 76.9 us on [4, 16, 2048,
+// 64]). A per-phase timeline shows why: the M phase of the four first waves
+// alone takes about 4200 cycles for 2048 cycles of MFMA work. Issuing the
+// tile loads costs about 1250 of them, and the P V part is held to the rate
+// of the transposed LDS reads. When the two phases overlap, the X phase
+// slows from about 1950 to 3300 cycles. So a step costs about as much as
+// the two phases back to back.
 // cfg selects the alternatives for timing comparisons. cfg 7 and 8 are the
 // tile that "What the tiling is actually constrained by" derives from the
 // on-chip memory ("The formula, which the title only gestures at"):
@@ -757,6 +1095,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
       case 4: return launch_fwd_bf16_cfg<128, 1, 4, 64>(a, mask, stream);
       case 7: return launch_fwd_bf16_cfg<128, 1, 4, 160, 1>(a, mask, stream);
       case 8: return launch_fwd_bf16_xb<128, 160>(a, mask, stream);
+      case 9: return launch_fwd_bf16_pp<128, 1, 128>(a, mask, stream);
       default:
         if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<128, 1, 4, 32>(a, mask, stream);
         return launch_fwd_bf16_cfg<128, 1, 8, 128>(a, mask, stream);
@@ -773,6 +1112,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mask, int cfg, hipStream
       return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
     case 7: return launch_fwd_bf16_cfg<64, 1, 2, 320, 1>(a, mask, stream);
     case 8: return launch_fwd_bf16_xb<64, 320>(a, mask, stream);
+    case 9: return launch_fwd_bf16_pp<64, 2, 64>(a, mask, stream);
     default:
       if (mask == MASK_NONE) return launch_fwd_bf16_cfg<64, 2, 8, 64>(a, mask, stream);
       if (mask == MASK_LOCAL) return launch_fwd_bf16_cfg<64, 1, 4, 32>(a, mask, stream);

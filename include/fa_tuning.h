@@ -21,6 +21,9 @@
  *            7 = 32 x 4, 160 keys (the derived tile: B_c = ceil(M / 4d) with
  *                M = 160 KiB of LDS in bf16 elements, B_r = 128);
  *            8 = 32 x 8, 160 keys (the derived B_c with the default 256 rows);
+ *            9 = ping-pong schedule, 32 x 8, 128 keys (the two waves of each
+ *                SIMD one phase apart: one on the matrix core while the
+ *                other runs the softmax);
  *            5, 6 = the default.
  *   d = 64:  1 = 32 x 8, 64 keys;  2 = block-pipelined 32 x 8, 128 keys;
  *            3 = 32 x 8, 128 keys;  4 = 32 x 4, 64 keys;
@@ -28,7 +31,8 @@
  *            6 = 64 x 4 or 64 x 8 (the workgroup size the mask does not pick);
  *            7 = 32 x 2, 320 keys (the derived tile at d = 64: B_c = 320,
  *                B_r = 64);
- *            8 = 64 x 4, 320 keys (the derived B_c with 256 rows).
+ *            8 = 64 x 4, 320 keys (the derived B_c with 256 rows);
+ *            9 = ping-pong schedule, 64 x 8, 64 keys.
  *   float32: only cfg = 0.
  * Backward, bf16: 2 = the other workgroup size (4 or 8 waves) than the mask
  *   picks; float32: only cfg = 0.

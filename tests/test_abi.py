@@ -139,7 +139,7 @@ def test_tuned_entry_points_reject_unknown_cfg(lib):
     o, lse = ctypes.c_void_p(0x200000), ctypes.c_void_p(0x900000)
     def tf(cfg, dtype=1, d=64, q=FAKE):
         return lib.fa_fwd_tuned(q, FAKE, FAKE, o, lse, 1, 1, 8, d, dtype, 0.125, 0, 0, cfg, None)
-    assert tf(-1) == 11 and tf(9) == 11 and tf(1 << 20) == 11
+    assert tf(-1) == 11 and tf(10) == 11 and tf(1 << 20) == 11
     assert tf(3, dtype=0, d=8) == 11
     assert tf(0, q=None) == 1 and tf(5, q=None) == 1  # a known cfg goes on to validation
     p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]

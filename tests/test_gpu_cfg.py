@@ -31,7 +31,7 @@ FWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("shape,mask,window,mult", FWD_CASES,
                          ids=[f"{s}-{m}-{w}-x{k:g}" for s, m, w, k in FWD_CASES])
 def test_fwd_cfg(cfg, shape, mask, window, mult):
@@ -44,6 +44,19 @@ def test_fwd_cfg(cfg, shape, mask, window, mult):
                                         ((1, 2, 1000, 64), "causal")])
 def test_fwd_derived_tile_long(cfg, shape, mask):
     fwd_case(shape, BF16, mask, 0, seed=cfg + shape[2], cfg=cfg)
+
+
+# cfg 9 (ping-pong schedule): an odd and an even number of key tiles, one
+# tile, the band, and rows past the last full workgroup
+@pytest.mark.parametrize("shape,mask,window", [((1, 2, 1000, 128), "causal", 0),
+                                               ((1, 2, 1100, 128), "none", 0),
+                                               ((1, 1, 100, 128), "none", 0),
+                                               ((1, 2, 1500, 128), "local", 200),
+                                               ((1, 2, 1000, 64), "causal", 0),
+                                               ((1, 1, 1401, 64), "none", 0),
+                                               ((1, 2, 999, 64), "local", 100)])
+def test_fwd_pingpong_long(shape, mask, window):
+    fwd_case(shape, BF16, mask, window, seed=9 + shape[2], cfg=9)
 
 
 BWD_CASES = [
@@ -64,7 +77,7 @@ def test_bwd_cfg(shape, mask, window):
 def test_unknown_cfg_rejected():
     q = torch.zeros((1, 1, 8, 64), dtype=BF16, device="cuda")
     o, lse = torch.empty_like(q), torch.empty((1, 1, 8), dtype=torch.float32, device="cuda")
-    for bad in (-1, 9, 100):
+    for bad in (-1, 10, 100):
         with pytest.raises(FAError):
             fa_fwd_tuned(q, q.clone(), q.clone(), o, lse, 0.125, None, 0, bad)
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
