@@ -127,6 +127,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
     q_hi = hh < N ? (int)hh : N;
   }
   const int t_begin = q_lo / BRQ, t_end = q_lo < q_hi ? (q_hi + BRQ - 1) / BRQ : t_begin;
+  const int n_t = t_end - t_begin;
+  // i-th query tile visited: in index order, except under the band mask
+  // (rotated so that neighbouring workgroups read shared tiles together)
+  const int t_rot = MASK == MASK_LOCAL ? band_tile_rotation(BC, BRQ, a.window, t_begin, n_t) : 0;
+  auto tile_at = [&](int i) {
+    if constexpr (MASK != MASK_LOCAL) return t_begin + i;
+    const int j = i + t_rot;
+    return t_begin + (j >= n_t ? j - n_t : j);
+  };
   // query rows that can see this wave's keys
   int wq_lo = 0, wq_hi = N;
   if (MASK == MASK_CAUSAL) wq_lo = kw0;
@@ -193,9 +202,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
     }
   };
 
-  if (t_begin < t_end) {
-    dma(t_begin, 0);
-    ld_stats(t_begin);
+  if (n_t > 0) {
+    dma(tile_at(0), 0);
+    ld_stats(tile_at(0));
     st_stats(0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V rows and the first tile are in LDS
@@ -206,15 +215,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
   const int tr_ch8 = 4 * (g16 & 1) + (s16 & 3);
   const int vrow = wv * 32 + l32;  // this lane's V row in sVt
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
+  for (int i = 0; i < n_t; ++i) {
+    const int buf = i & 1;
     const char* sQ = sQO + buf * QTILEB;
     const char* sO = sQO + (2 + buf) * QTILEB;
-    if (t + 1 < t_end) {
-      dma(t + 1, buf ^ 1);
-      ld_stats(t + 1);
+    if (i + 1 < n_t) {
+      dma(tile_at(i + 1), buf ^ 1);
+      ld_stats(tile_at(i + 1));
     }
-    const int q0 = t * BRQ;
+    const int q0 = tile_at(i) * BRQ;
 #pragma unroll 1
     for (int qb = 0; qb < QBN; ++qb) {
       const int qr0 = q0 + qb * 32;
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv2_bf16_kernel(BwdArgs a) {
         }
       }
     }
-    if (t + 1 < t_end) st_stats(buf ^ 1);
+    if (i + 1 < n_t) st_stats(buf ^ 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed in LDS
     __syncthreads();
   }
@@ -396,6 +405,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   int k_lo, k_hi;
   key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
   const int t_begin = k_lo / BC, t_end = (k_hi + BC - 1) / BC;
+  const int n_t = t_end - t_begin;
+  // i-th key tile visited (rotated under the band mask, as in the dK/dV kernel)
+  const int t_rot = MASK == MASK_LOCAL ? band_tile_rotation(BR, BC, a.window, t_begin, n_t) : 0;
+  auto tile_at = [&](int i) {
+    if constexpr (MASK != MASK_LOCAL) return t_begin + i;
+    const int j = i + t_rot;
+    return t_begin + (j >= n_t ? j - n_t : j);
+  };
   int wk_lo, wk_hi;
   key_range<MASK>(qw0, qw0 + 32, N, a.window, wk_lo, wk_hi);
   const bool wave_live = qw0 < N;
@@ -441,7 +458,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
       }
     }
   };
-  if (t_begin < t_end) dma(t_begin, 0);
+  if (n_t > 0) dma(tile_at(0), 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
@@ -451,12 +468,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
 
   // the tile loop unrolled by two, so that the double-buffer index is a
   // compile-time constant (LDS addresses take it as an immediate offset)
-  auto tile_step = [&](int t, auto buf_tag) {
+  auto tile_step = [&](int i, auto buf_tag) {
     constexpr int buf = decltype(buf_tag)::value;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
-    if (t + 1 < t_end) dma(t + 1, buf ^ 1);
-    const int k0 = t * BC;
+    if (i + 1 < n_t) dma(tile_at(i + 1), buf ^ 1);
+    const int k0 = tile_at(i) * BC;
     if (wave_live && k0 < wk_hi && k0 + BC > wk_lo) {
       bf16x8 dsb[KB][2];
 #pragma unroll
@@ -519,9 +536,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed in LDS
     __syncthreads();
   };
-  for (int t = t_begin; t < t_end; t += 2) {
-    tile_step(t, ic<0>{});
-    if (t + 1 < t_end) tile_step(t + 1, ic<1>{});
+  for (int i = 0; i < n_t; i += 2) {
+    tile_step(i, ic<0>{});
+    if (i + 1 < n_t) tile_step(i + 1, ic<1>{});
   }
 
   if (qi < N) {

@@ -105,6 +105,23 @@ __device__ __forceinline__ void key_range(int q0, int q1, int N, int window, int
   }
 }
 
+// Visiting order of a workgroup's key tiles under the band mask. A
+// workgroup of br query rows starting at a multiple of br needs the
+// p = ceil((br + window) / bc) + ceil(window / bc) key tiles around its rows
+// (fewer at the sequence ends), and its neighbours need most of the same
+// tiles. Walked from its own first tile, a workgroup reaches a tile some
+// steps after its neighbour did, by which time the L2 of an XCD running
+// ~160 such workgroups has evicted it. Walked instead by tile index modulo
+// p, starting at the tile whose index is a multiple of p (a rotation of the
+// contiguous range), every workgroup reads tile t at step t mod p, so
+// neighbours that run together read each shared tile together. Returns the
+// rotation, in tiles, of the range [t_begin, t_begin + n_t).
+__device__ __forceinline__ int band_tile_rotation(int br, int bc, int window, int t_begin, int n_t) {
+  const int p = (br + window + bc - 1) / bc + (window + bc - 1) / bc;
+  const int first = (p - t_begin % p) % p;  // first tile index that is a multiple of p
+  return first < n_t ? first : 0;
+}
+
 // Whether every (query, key) pair with query in [q0, q1) and key in
 // [k0, k1) is allowed (so the tile needs no per-element mask).
 template <int MASK>

@@ -125,6 +125,15 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
   key_range<MASK>(q0, q0 + BR, N, a.window, k_lo, k_hi);
   const int t_begin = k_lo / BC;
   const int t_end = (k_hi + BC - 1) / BC;
+  const int n_t = t_end - t_begin;
+  // i-th key tile visited: in index order, except under the band mask
+  // (rotated so that neighbouring workgroups read shared tiles together)
+  const int t_rot = MASK == MASK_LOCAL ? band_tile_rotation(BR, BC, a.window, t_begin, n_t) : 0;
+  auto tile_at = [&](int i) {
+    if constexpr (MASK != MASK_LOCAL) return t_begin + i;
+    const int j = i + t_rot;
+    return t_begin + (j >= n_t ? j - n_t : j);
+  };
   int wk_lo, wk_hi;
   key_range<MASK>(qw0, qw0 + QW, N, a.window, wk_lo, wk_hi);
   const bool wave_live = qw0 < N;
@@ -185,8 +194,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  if (t_begin < t_end) {
-    dma(t_begin, 0);
+  if (n_t > 0) {
+    dma(tile_at(0), 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile is in LDS
   }
   __syncthreads();
@@ -200,12 +209,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
 
   // the tile loop unrolled by two, so that the double-buffer index is a
   // compile-time constant (LDS addresses take it as an immediate offset)
-  auto tile_step = [&](int t, auto buf_tag) {
+  auto tile_step = [&](int i, auto buf_tag) {
     constexpr int buf = decltype(buf_tag)::value;
     const char* sK = smem + buf * TILEB;
     const char* sV = smem + (2 + buf) * TILEB;
-    if (t + 1 < t_end) dma(t + 1, buf ^ 1);
-    const int k0 = t * BC;
+    if (i + 1 < n_t) dma(tile_at(i + 1), buf ^ 1);
+    const int k0 = tile_at(i) * BC;
 
     // Skip tiles that hold no allowed key for any row of this wave.
     if (wave_live && k0 < wk_hi && k0 + BC > wk_lo) {
@@ -370,9 +379,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void fwd_bf16_kernel(FwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed in LDS
     __syncthreads();
   };
-  for (int t = t_begin; t < t_end; t += 2) {
-    tile_step(t, ic<0>{});
-    if (t + 1 < t_end) tile_step(t + 1, ic<1>{});
+  for (int i = 0; i < n_t; i += 2) {
+    tile_step(i, ic<0>{});
+    if (i + 1 < n_t) tile_step(i + 1, ic<1>{});
   }
 
   // ---- epilogue: O = acc / (sum of the rounded weights), LSE = m * scale + ln l
