@@ -20,6 +20,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --std-sweep [--std-n N] [--no-settle]
                                       (fused fa_fwd vs standard fa_fwd_standard, N = 1k..16k)
        python bench.py --summarize-std DIR   (their HBM bytes from per-N counter passes, no GPU)
+       python bench.py --oracle-all   (the CPU oracle on every workload of the statement, no GPU)
        python bench.py --km-sweep [--km-n N] [--km-bc BC] [--no-settle]
                                       (key-major fa_fwd_keymajor over its key-block sizes)
        python bench.py --summarize-km DIR    (its HBM bytes vs block size, no GPU)
@@ -230,6 +231,9 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true",
                     help="every forward kernel shape (fa_fwd_tuned cfg 0..8) on the causal "
                          "[2,16,8192,128] and unmasked [4,16,2048,64] workloads; markdown table")
+    ap.add_argument("--oracle-all", action="store_true",
+                    help="time the CPU oracle (dense and tiled forward; dense backward where the "
+                         "workload has one) on every workload of the statement; no GPU")
     ap.add_argument("--sweep", action="store_true",
                     help="time fa_fwd and fa_bwd over N = 2048..16384 (B = 32768/N, H = 16), "
                          "d in {64, 128}, mask in {none, causal}; prints a markdown table")
@@ -249,6 +253,9 @@ def main():
         return
     if args.summarize_util:
         print(summarize_util(args.summarize_util))
+        return
+    if args.oracle_all:
+        print(oracle_all())
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: runs on one GPU only (heads shard across GPUs without "
@@ -1076,6 +1083,62 @@ def cpu_baseline(w, inp, have_bwd, target_s=12.0):
             "sample": f"{n} of {B * H} (b,h) slices [1,1,{N},{d}] of {w.name}: dense forward"
                       + (" + dense backward" if have_bwd else "")
                       + " (value); tiled forward 128x128 timed beside; float64, OpenMP"}
+
+
+# The five workloads of the statement, in its order (c1 .. c5).
+STATEMENT_WORKLOADS = ("toy_fp32_n6_d4", "bf16_b4h16_n2048_d64", "bf16_causal_b2h16_n8192_d128",
+                       "bf16_local128_x8_b1h32_n16384_d128", "bf16_causal_bwd_b2h16_n4096_d128")
+
+
+def oracle_all(target_s=6.0):
+    """The CPU oracle as it stands on every workload of the statement: per
+    workload, consecutive (batch, head) slices until about target_s seconds,
+    each through the dense forward, the tiled online forward (128 x 128 tiles;
+    2 x 2 on the 6-row toy) and, where the workload has a backward, the dense
+    backward. Rates use the bench's FLOP formulas; the whole-workload time is
+    the per-slice mean times the slice count. Markdown on stdout."""
+    import oracle
+    from exact_tiled_attention_fwd_amd.synth import WORKLOADS, make_inputs
+    out = [f"Host: {cpu_model()}; {os.cpu_count()} CPUs visible; the oracle ran with "
+           f"{omp_threads()} OpenMP threads.", "",
+           "| Config | Workload | Slices timed | Dense fwd s/slice | Dense fwd GFLOP/s "
+           "| Tiled fwd s/slice | Tiled fwd GFLOP/s | Dense bwd s/slice | Dense bwd GFLOP/s "
+           "| Whole workload (dense), s |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    toy = make_inputs(WORKLOADS["toy_fp32_n6_d4"])  # first call loads the library: untimed
+    oracle.fwd_dense(toy["q"], toy["k"], toy["v"], 0.5, "none", 0)
+    for ci, name in enumerate(STATEMENT_WORKLOADS, 1):
+        w = WORKLOADS[name]
+        has_bwd = name == "bf16_causal_bwd_b2h16_n4096_d128"
+        inp = make_inputs(w, with_dout=has_bwd)
+        B, H, N, d = w.shape
+        keys = ("q", "k", "v", "dout") if has_bwd else ("q", "k", "v")
+        flat = {k_: inp[k_].reshape(B * H, N, d) for k_ in keys}
+        one = type(w)(**{**w.__dict__, "B": 1, "H": 1})
+        tile = 128 if N >= 128 else 2
+        td = tt = tb = 0.0
+        n = 0
+        t0 = time.perf_counter()
+        while n < B * H and (n == 0 or time.perf_counter() - t0 < target_s):
+            sl = {k_: t[n:n + 1] for k_, t in flat.items()}
+            a = time.perf_counter()
+            oracle.fwd_dense(sl["q"], sl["k"], sl["v"], w.scale, w.mask, w.window)
+            b = time.perf_counter()
+            oracle.fwd_tiled(sl["q"], sl["k"], sl["v"], w.scale, tile, tile, w.mask, w.window)
+            c = time.perf_counter()
+            if has_bwd:
+                oracle.bwd_dense(sl["q"], sl["k"], sl["v"], sl["dout"], w.scale, w.mask, w.window)
+            td += b - a
+            tt += c - b
+            tb += time.perf_counter() - c
+            n += 1
+        ff, fb = fwd_flops(one), bwd_flops(one)
+        g = lambda flop, t: f"{flop * n / t / 1e9:.2f}" if t > 0 else "—"
+        bwd_cols = (f"{tb / n:.4g} | {g(fb, tb)}" if has_bwd else "— | —")
+        whole = (td + tb) / n * B * H
+        out.append(f"| c{ci} | `{name}` | {n} of {B * H} | {td / n:.4g} | {g(ff, td)} | "
+                   f"{tt / n:.4g} ({tile}×{tile}) | {g(ff, tt)} | {bwd_cols} | {whole:.4g} |")
+    return "\n".join(out)
 
 
 if __name__ == "__main__":

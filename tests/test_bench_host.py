@@ -134,3 +134,17 @@ def test_cpu_baseline_keys(bench):
     fb = 2.5 * ff
     assert abs(r["value"] - (ff + fb) / (r["dense_fwd_s"] + r["dense_bwd_s"]) / 1e12) <= \
         1e-6 + 1e-2 * r["value"]
+
+
+def test_oracle_all_covers_every_workload(bench):
+    """bench.py --oracle-all: one row per workload of the statement, in
+    order, each with at least one slice timed and the backward only on c5."""
+    text = bench.oracle_all(target_s=0.0)
+    rows = [ln for ln in text.splitlines() if ln.startswith("| c")]
+    assert [r.split("|")[1].strip() for r in rows] == ["c1", "c2", "c3", "c4", "c5"]
+    for r, name in zip(rows, bench.STATEMENT_WORKLOADS):
+        cells = [c.strip() for c in r.split("|")[1:-1]]
+        assert cells[1] == f"`{name}`" and cells[2].startswith("1 of ")
+        assert float(cells[3]) > 0 and float(cells[5].split()[0]) > 0
+        assert (cells[7] != "—") == (name == "bf16_causal_bwd_b2h16_n4096_d128")
+    assert f"{bench.omp_threads()} OpenMP threads" in text
