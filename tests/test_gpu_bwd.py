@@ -181,3 +181,17 @@ def test_full_size_band_backward():
     sv = (dvf.sum(dim=2) - dof.sum(dim=2)).norm() / dof.sum(dim=2).norm()
     print(f"invariants: |sum dK|/|dK| = {float(sk):.2e}, |sum dV - sum dO| rel = {float(sv):.2e}")
     assert float(sk) <= 2e-2 and float(sv) <= 1e-2
+
+
+# Under the band mask every kernel visits its tiles in a rotated order (by tile
+# index modulo the tile count of an interior window). These lengths give
+# dozens of interior workgroups with every rotation offset, plus ragged ends;
+# radii that are not multiples of any tile size, at both head dimensions.
+BAND_ROTATION_CASES = [((1, 2, 2500, 128), 31), ((1, 2, 2500, 128), 200),
+                       ((1, 2, 3001, 64), 33), ((1, 2, 3001, 64), 300)]
+
+
+@pytest.mark.parametrize("shape,window", BAND_ROTATION_CASES,
+                         ids=[f"{s}-w{w}" for s, w in BAND_ROTATION_CASES])
+def test_band_backward_rotated_order(shape, window):
+    run_case(shape, BF16, "local", window, seed=shape[2] + window)

@@ -159,3 +159,11 @@ def test_full_size_whole_tensor(name):
     B, H, N, d = w.shape
     print(f"{name}: max|dO|={eo:.3e} max|dLSE|={el:.3e} over all {B * H * N} rows "
           f"(oracle {t_or:.1f} s on the host)", flush=True)
+
+
+# The band forward's rotated key-tile order (see the backward's test of the
+# same name): many interior workgroups, ragged ends, odd radii, both d.
+@pytest.mark.parametrize("shape,window", [((1, 2, 2500, 128), 31), ((1, 2, 2500, 128), 200),
+                                          ((1, 2, 3001, 64), 33), ((1, 2, 3001, 64), 300)])
+def test_band_forward_rotated_order(shape, window):
+    run_case(shape, BF16, "local", window, seed=shape[2] + window + 1)
