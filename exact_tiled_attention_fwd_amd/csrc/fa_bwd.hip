@@ -24,6 +24,11 @@
 // Recomputing S and dP in the dQ kernel costs two extra contractions (7
 // instead of the 5 the gradient needs), the price of determinism without
 // atomics. The float32 path keeps a separate preprocess launch for D.
+// Under the band mask both kernels visit their tiles in a rotated order (by
+// tile index modulo the window's tile count), so that neighbouring
+// workgroups read each shared tile at the same step, and the dK/dV kernel
+// takes its key blocks in descending order, opposite to the dQ kernel
+// launched just before it.
 #include "fa_common.h"
 #include "fa_kernels.h"
 #include "fa_tile_ops.h"

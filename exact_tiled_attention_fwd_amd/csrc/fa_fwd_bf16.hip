@@ -26,11 +26,17 @@
 //    are bank-conflict free; the next tile's global loads are in flight
 //    while the current one is computed.
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
-//  * Two schedules: the tile kernel runs all scores of a K tile, then the
+//  * Three schedules: the tile kernel runs all scores of a K tile, then the
 //    softmax, then P V with the exp of the next 32-key block interleaved;
 //    the block-pipelined kernel (an alternative) overlaps the scores of
 //    block b+1 with the exp of block b and P V of block b with the maximum
-//    of block b+1, keeping the online-softmax state per 32-key block.
+//    of block b+1, keeping the online-softmax state per 32-key block; the
+//    ping-pong kernel (another alternative) runs the two waves of each SIMD
+//    one phase apart, one on the matrix core while the other runs the
+//    softmax.
+//  * Under the band mask the key tiles are visited in a rotated order (by
+//    tile index modulo the window's tile count), so that neighbouring
+//    workgroups read each shared tile at the same step.
 //  * The subtracted maximum is refreshed lazily: the reference m only moves
 //    when some row's tile maximum exceeds it by more than 2^RESCALE_LOG2 in
 //    exp2 units, so most tiles skip the rescale of the accumulator (p then
@@ -717,9 +723,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_xb_kernel(FwdArgs a) {
 // (bf16) until the next M phase.
 // LDS: K of tile t is read in the M(t) phases of both waves, V of tile t in
 // their M(t+1) phases, so the loads of K(t+1) and V(t) share one window of
-// two phases: issued at the start of the first wave's M(t) phase (the second
-// wave issues its part at the same moment, in its X(t-1) phase), waited for
-// before the barrier that ends that window.
+// two phases: the first wave of each SIMD issues all of them at the start of
+// its M(t) phase and waits for them before the barrier that ends its X(t).
 template <int D, int QB, int BC, int MASK>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
   constexpr int NW = 8;
