@@ -73,6 +73,10 @@ typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_LOCAL = 2 } fa_mask
  *   lse     : output [B][H][N] float32: LSE_i = m_i + ln l_i in natural-log
  *             units of the scaled, masked logits (m_i the row maximum, l_i the
  *             row sum of exp(z_ij - m_i)); the backward pass consumes it.
+ * With FA_BF16 the weights are rounded to bfloat16 before they multiply V,
+ * and each output row is divided by the float32 sum of those rounded
+ * weights, so that it is a convex combination of value rows up to float32
+ * rounding; LSE keeps the sum of the unrounded weights.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, fa_dtype dtype,
